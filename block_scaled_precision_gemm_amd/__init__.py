@@ -1,0 +1,201 @@
+"""Python binding of the block-scaled GEMM C ABI (libbsg.so, include/bsg.h).
+
+Argument marshalling only: every step of the GEMM runs in the HIP library.  Tensors are passed as
+device pointers (anything with .data_ptr(), or a plain int); streams as hipStream_t handles (an
+object with .cuda_stream, an int, or None for torch's current stream).  PyTorch is only used, when
+present, to find the current stream.
+
+The library is loaded on first use and a missing build raises LibraryNotBuilt: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_e4m3", "decode_nvfp4",
+           "FORMATS", "OUT_DTYPES", "abi_version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsg.so")
+
+FORMATS = {"mxfp8": 1, "nvfp4": 2}
+OUT_DTYPES = {"bf16": 1, "f16": 2}
+EPI_BIAS, EPI_SILU = 1, 2
+
+STATUS = {0: "BSG_OK", 1: "BSG_ERR_NULL", 2: "BSG_ERR_SHAPE", 3: "BSG_ERR_UNSUPPORTED", 4: "BSG_ERR_ALIGN",
+          5: "BSG_ERR_DEVICE", 6: "BSG_ERR_HIP", 7: "BSG_ERR_ALLOC", 8: "BSG_ERR_ABI"}
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class BsgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("format", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("device", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("variant", ctypes.c_char * 64), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("grid_x", ctypes.c_uint32),
+                ("grid_y", ctypes.c_uint32), ("grid_z", ctypes.c_uint32), ("block_x", ctypes.c_uint32),
+                ("lds_bytes", ctypes.c_uint32), ("workspace_bytes", ctypes.c_uint64)]
+
+
+_lib = None
+
+_VP = ctypes.c_void_p
+_SIGNATURES = {
+    "bsg_plan_create": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.POINTER(_VP)]),
+    "bsg_run": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP]),
+    "bsg_run_alpha_ptr": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "bsg_plan_destroy": (ctypes.c_int, [_VP]),
+    "bsg_plan_query": (ctypes.c_int, [_VP, ctypes.POINTER(PlanInfo)]),
+    "bsg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "bsg_last_error": (ctypes.c_char_p, []),
+    "bsg_abi_version": (ctypes.c_int, []),
+    "bsg_test_decode_e4m3": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP]),
+    "bsg_test_decode_nvfp4": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int64, _VP]),
+    "bsg_bench_loop": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.POINTER(_VP), ctypes.POINTER(_VP),
+                                      ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.POINTER(_VP),
+                                      ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_VP), ctypes.c_int,
+                                      ctypes.c_int, _VP, ctypes.POINTER(ctypes.c_double)]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libbsg.so (once).  Raises LibraryNotBuilt if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise LibraryNotBuilt(f"{path} is missing: build it with `python -m block_scaled_precision_gemm_amd.build` "
+                              "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().bsg_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise BsgError(status, load_library().bsg_last_error().decode(errors="replace"))
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return torch.cuda.current_stream().cuda_stream
+        except ImportError:
+            pass
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+class Plan:
+    """A cached GEMM plan: D = epi(alpha * A x B^T (+ bias)) for one problem shape and variant."""
+
+    def __init__(self, fmt: str, M: int, N: int, K: int, out: str = "bf16", bias: bool = False,
+                 silu: bool = False, device: int = -1):
+        lib = load_library()
+        self._lib = lib
+        self._h = None
+        self.fmt, self.M, self.N, self.K, self.out, self.bias, self.silu = fmt, M, N, K, out, bias, silu
+        prob = Problem(ctypes.sizeof(Problem), FORMATS[fmt], OUT_DTYPES[out],
+                       (EPI_BIAS if bias else 0) | (EPI_SILU if silu else 0), M, N, K, device)
+        h = _VP()
+        _check(lib.bsg_plan_create(ctypes.byref(prob), ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self) -> int:
+        return self._h.value
+
+    def run(self, A, B, sA, sB, D, alpha: float = 1.0, bias=None, stream=None) -> None:
+        _check(self._lib.bsg_run(self._h, _ptr(A), _ptr(B), _ptr(sA), _ptr(sB), _ptr(bias), float(alpha), _ptr(D),
+                                 _stream(stream)))
+
+    def run_alpha_ptr(self, A, B, sA, sB, D, alpha_dev, bias=None, stream=None) -> None:
+        _check(self._lib.bsg_run_alpha_ptr(self._h, _ptr(A), _ptr(B), _ptr(sA), _ptr(sB), _ptr(bias),
+                                           _ptr(alpha_dev), _ptr(D), _stream(stream)))
+
+    def info(self) -> dict:
+        inf = PlanInfo()
+        inf.struct_size = ctypes.sizeof(PlanInfo)
+        _check(self._lib.bsg_plan_query(self._h, ctypes.byref(inf)))
+        return dict(variant=inf.variant.decode(), tile=(inf.tile_m, inf.tile_n, inf.tile_k),
+                    grid=(inf.grid_x, inf.grid_y, inf.grid_z), block=inf.block_x, lds_bytes=inf.lds_bytes,
+                    workspace_bytes=inf.workspace_bytes)
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            _check(self._lib.bsg_plan_destroy(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def bench_loop(plan: Plan, sets: list[dict], calls_per_set: int, mode: int, stream) -> float:
+    """Native loop of len(sets) * calls_per_set bsg_run calls; returns the host wall time in us.
+
+    Each set is a dict with A, B, sA, sB, D, alpha and optional bias.  mode 0 = direct calls,
+    mode 1 = one HIP graph per set (captured outside the timed region) replayed.
+    """
+    lib = load_library()
+    n = len(sets)
+    arr = lambda key: (_VP * n)(*[_ptr(s.get(key)) for s in sets])  # noqa: E731
+    alphas = (ctypes.c_float * n)(*[float(s["alpha"]) for s in sets])
+    has_bias = any(s.get("bias") is not None for s in sets)
+    wall = ctypes.c_double()
+    _check(lib.bsg_bench_loop(plan._h, n, arr("A"), arr("B"), arr("sA"), arr("sB"), arr("bias") if has_bias else None,
+                              alphas, arr("D"), calls_per_set, mode, _stream(stream), ctypes.byref(wall)))
+    return wall.value
+
+
+def decode_e4m3(codes, out, stream=None) -> None:
+    """out[i] (fp32) = device decode of E4M3 code codes[i] (test entry point)."""
+    n = codes.numel() if hasattr(codes, "numel") else len(codes)
+    _check(load_library().bsg_test_decode_e4m3(_ptr(codes), _ptr(out), n, _stream(stream)))
+
+
+def decode_nvfp4(packed, scale_codes, out_bf16, n_elements: int, stream=None) -> None:
+    """out_bf16[k] = device dequantisation of NVFP4 element k (packed[k/2] nibble, scale_codes[k/16])."""
+    _check(load_library().bsg_test_decode_nvfp4(_ptr(packed), _ptr(scale_codes), _ptr(out_bf16), n_elements,
+                                                _stream(stream)))

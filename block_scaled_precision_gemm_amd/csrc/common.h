@@ -1,0 +1,55 @@
+// Shared host/device definitions of the block-scaled GEMM kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+// MFMA operand/accumulator register vectors.
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+enum class Fmt : int { MXFP8 = 1, NVFP4 = 2 };
+enum class Out : int { BF16 = 1, F16 = 2 };
+
+// Kernel arguments, filled once at plan time; the per-call pointers and alpha are patched into a
+// copy by the run entry point.  Passed by value (kernarg segment).
+struct GemmArgs {
+  const uint8_t* A;       // MXFP8: [M][K] E4M3; NVFP4: [M][K/2] packed E2M1
+  const uint8_t* B;       // MXFP8: [N][K] E4M3; NVFP4: [N][K/2] packed E2M1
+  const uint8_t* sA;      // MXFP8: [M][K/32] E8M0; NVFP4: [M][K/16] E4M3
+  const uint8_t* sB;      // MXFP8: [N][K/32] E8M0; NVFP4: [N][K/16] E4M3
+  const float* bias;      // [N] fp32 or null
+  const float* alpha_ptr; // device alpha, or null to use `alpha`
+  void* D;                // [M][N] bf16/fp16
+  float alpha;
+  int M, N, K;
+  int tiles_m, tiles_n;   // output tile grid
+};
+
+// A launcher: enqueues one kernel on `stream` with a precomputed launch shape.
+typedef hipError_t (*LaunchFn)(const GemmArgs& args, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream);
+
+struct KernelVariant {
+  const char* name;
+  LaunchFn launch;
+  int tile_m, tile_n, tile_k;
+  int block_threads;
+  uint32_t lds_bytes;
+};
+
+// Variant tables, one per format: index = out dtype (0 bf16, 1 f16) * 4 + bias * 2 + silu.
+// Each kernel family returns its table for the M bucket it serves.
+const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K);
+const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K);
+
+inline int variant_index(Out out, bool bias, bool silu) {
+  return (out == Out::F16 ? 4 : 0) + (bias ? 2 : 0) + (silu ? 1 : 0);
+}
+
+}  // namespace bsg

@@ -1,0 +1,146 @@
+/*
+ * bsg.h -- block-scaled GEMM for AMD MI355X (gfx950), C ABI.
+ *
+ * Computes, on one GPU,
+ *
+ *     D[m][n] = epi( alpha * sum_k a[m][k] * b[n][k] + bias[n] )
+ *
+ * where a and b are the dequantised operands, epi is SiLU or the identity,
+ * accumulation is fp32 and D is written as BF16 or FP16.  This is the
+ * operation of the nvFuser PR #5736 page ("Add Cutlass MxFp8 Block Scale
+ * Matrix Multiplication": mxfp8_scaled_mm, "compute C = alpha * A @ B",
+ * A RowMajor, B ColumnMajor i.e. stored N x K, fp32 accumulator, FP16/BF16
+ * output) and of the CUTLASS issue #3003 page (runNvfp4Gemm<T, kEnableSilu,
+ * kEnableBias>(output, a, b, scales_a, scales_b, bias, float alpha, M, N, K,
+ * stream)).
+ *
+ * Operand formats (element types as OCP Microscaling v1.0 defines them):
+ *   BSG_FMT_MXFP8: A uint8[M][K] E4M3 codes, row-major; B uint8[N][K] E4M3,
+ *                  K contiguous; sA uint8[M][K/32], sB uint8[N][K/32] E8M0
+ *                  scale codes, one per 32 consecutive K elements, block b
+ *                  covering k in [32b, 32b+32).
+ *   BSG_FMT_NVFP4: A uint8[M][K/2], B uint8[N][K/2] packed E2M1, element 2t
+ *                  in the low nibble of byte t; sA uint8[M][K/16],
+ *                  sB uint8[N][K/16] E4M3 scale codes, one per 16 K elements.
+ * Scale tensors are plain row-major [rows][K/block] (no padding, no swizzle).
+ * bias: float[N] (fp32), broadcast over rows.  D: bf16/fp16 [M][N] row-major.
+ * All operand pointers are device pointers.
+ *
+ * Life cycle (the per-call work that the issue #3003 page measures as 534 of
+ * 625 us per call -- argument building, workspace allocation, can_implement,
+ * descriptor initialisation -- is done once, in bsg_plan_create):
+ *   bsg_plan_create(problem)  once: validates, picks the kernel variant,
+ *                             precomputes grid and kernel arguments.
+ *   bsg_run(plan, ...)        per call: O(1) pointer checks and one kernel
+ *                             launch on the caller's stream.  No allocation,
+ *                             no synchronisation, no device query, so it may
+ *                             be captured into a HIP graph.
+ *   bsg_plan_destroy(plan)    frees the plan (host memory only).
+ *
+ * Ownership: the caller owns every operand buffer, D and the stream; the
+ * library owns the plan.  A plan is immutable after creation: concurrent
+ * bsg_run calls on one plan from several threads/streams are safe.
+ *
+ * Errors: every function returns a bsg_status and never throws or aborts.
+ * On failure nothing is launched and bsg_last_error() (thread-local) holds a
+ * message.
+ */
+#ifndef BSG_H
+#define BSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSG_ABI_VERSION 1
+
+typedef enum bsg_status {
+  BSG_OK = 0,
+  BSG_ERR_NULL = 1,        /* a required pointer is NULL */
+  BSG_ERR_SHAPE = 2,       /* M, N or K out of range or not a multiple the format needs */
+  BSG_ERR_UNSUPPORTED = 3, /* valid request that no compiled kernel variant covers */
+  BSG_ERR_ALIGN = 4,       /* an operand pointer is not 16-byte aligned */
+  BSG_ERR_DEVICE = 5,      /* no device, or the device is not gfx950 */
+  BSG_ERR_HIP = 6,         /* a HIP runtime call failed (message holds hipGetErrorString) */
+  BSG_ERR_ALLOC = 7,       /* host allocation of the plan failed */
+  BSG_ERR_ABI = 8          /* struct_size mismatch or bad enum value */
+} bsg_status;
+
+typedef enum bsg_format {
+  BSG_FMT_MXFP8 = 1, /* E4M3 elements, E8M0 scale per 32 K */
+  BSG_FMT_NVFP4 = 2  /* packed E2M1 elements, E4M3 scale per 16 K, global fp32 alpha */
+} bsg_format;
+
+typedef enum bsg_out_dtype {
+  BSG_OUT_BF16 = 1,
+  BSG_OUT_F16 = 2
+} bsg_out_dtype;
+
+/* epilogue flags (kEnableBias / kEnableSilu of runNvfp4Gemm) */
+enum {
+  BSG_EPI_BIAS = 1u << 0, /* add bias[n] after alpha */
+  BSG_EPI_SILU = 1u << 1  /* y = x / (1 + exp(-x)) on x = alpha*acc (+ bias) */
+};
+
+typedef struct bsg_problem {
+  uint32_t struct_size; /* = sizeof(bsg_problem), else BSG_ERR_ABI */
+  int32_t format;       /* bsg_format */
+  int32_t out_dtype;    /* bsg_out_dtype */
+  uint32_t flags;       /* BSG_EPI_* */
+  int64_t M, N, K;      /* M >= 1; N >= 16, N % 16 == 0; K >= 32, K % 32 == 0 (MXFP8) or K % 16 == 0 (NVFP4) */
+  int32_t device;       /* HIP device ordinal; -1 = the current device at create time */
+} bsg_problem;
+
+typedef struct bsg_plan_s* bsg_plan; /* opaque, library-owned */
+
+typedef struct bsg_plan_info {
+  uint32_t struct_size; /* = sizeof(bsg_plan_info), set by the caller */
+  char variant[64];     /* kernel variant name */
+  int32_t tile_m, tile_n, tile_k;
+  uint32_t grid_x, grid_y, grid_z, block_x;
+  uint32_t lds_bytes;
+  uint64_t workspace_bytes; /* device workspace the plan owns (0: none) */
+} bsg_plan_info;
+
+/* Validate `problem`, choose the kernel variant for (format, out dtype, epilogue, M bucket) and
+ * precompute everything a call needs.  On success *out_plan is a new plan.  Errors: BSG_ERR_NULL,
+ * BSG_ERR_ABI, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED, BSG_ERR_DEVICE, BSG_ERR_HIP, BSG_ERR_ALLOC. */
+bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan);
+
+/* Enqueue D = epi(alpha * A x B^T (+ bias)) on `stream` (a hipStream_t; NULL = the null stream).
+ * A, B, sA, sB, D: device pointers laid out as described at the top of this file; A, B and D must be
+ * 16-byte aligned.  bias: device float[N], required iff the plan has BSG_EPI_BIAS (ignored otherwise).
+ * alpha: host fp32 value.  Returns after enqueueing (asynchronous).  Errors: BSG_ERR_NULL,
+ * BSG_ERR_ALIGN, BSG_ERR_HIP (launch failure). */
+bsg_status bsg_run(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB,
+                   const float* bias, float alpha, void* D, void* stream);
+
+/* Same as bsg_run, with alpha read by the kernel from device memory (the alpha_ptr form of the
+ * MXFP8 page's epilogue arguments).  alpha_dev: device pointer to one fp32. */
+bsg_status bsg_run_alpha_ptr(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB,
+                             const float* bias, const float* alpha_dev, void* D, void* stream);
+
+/* Free a plan.  NULL is accepted.  Kernels already enqueued with the plan are unaffected (their
+ * arguments were copied at launch). */
+bsg_status bsg_plan_destroy(bsg_plan plan);
+
+/* Describe the chosen variant.  info->struct_size must be sizeof(bsg_plan_info). */
+bsg_status bsg_plan_query(bsg_plan plan, bsg_plan_info* info);
+
+/* Static text for a status code. */
+const char* bsg_status_string(bsg_status s);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* bsg_last_error(void);
+
+/* BSG_ABI_VERSION of the built library. */
+int bsg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSG_H */

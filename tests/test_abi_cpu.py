@@ -1,0 +1,95 @@
+"""CPU-side checks of the C ABI library: it loads, exports every declared symbol, and validates
+requests before touching a device.  No compute call is made here."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_gemm_amd as bsg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(bsg_[a-z_0-9]+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bsg.load_library()
+    names = _declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), f"libbsg.so does not export {n}"
+
+
+def test_abi_version_and_status_strings():
+    lib = bsg.load_library()
+    assert lib.bsg_abi_version() == 1
+    for code, name in bsg.STATUS.items():
+        assert lib.bsg_status_string(code).decode() == name
+
+
+def _create(**kw):
+    prob = bsg.Problem(ctypes.sizeof(bsg.Problem), 1, 1, 0, 256, 256, 256, -1)
+    for k, v in kw.items():
+        setattr(prob, k, v)
+    h = ctypes.c_void_p()
+    st = bsg.load_library().bsg_plan_create(ctypes.byref(prob), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("struct_size", 8, 8), ("format", 3, 8), ("out_dtype", 0, 8), ("flags", 4, 8),
+    ("M", 0, 2), ("N", 0, 2), ("K", 0, 2), ("N", 250, 2), ("K", 48, 2), ("M", 1 << 31, 2),
+])
+def test_plan_create_validation(field, value, status):
+    st, h = _create(**{field: value})
+    assert st == status, bsg.load_library().bsg_last_error()
+    assert not h.value
+
+
+def test_nvfp4_k_rules():
+    st, _ = _create(format=2, K=40)
+    assert st == 2  # not a multiple of the 16-element block
+    st, _ = _create(format=2, K=48)
+    assert st == 3  # a valid NVFP4 K that no compiled kernel covers
+
+
+def test_valid_problem_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, h = _create()
+    assert st == 5 and not h.value
+    assert b"device" in bsg.load_library().bsg_last_error().lower()
+
+
+def test_null_arguments():
+    lib = bsg.load_library()
+    assert lib.bsg_plan_create(None, None) == 1
+    assert lib.bsg_run(None, 1, 1, 1, 1, None, 1.0, 1, None) == 1
+    assert lib.bsg_plan_destroy(None) == 0
+    assert lib.bsg_plan_query(None, None) == 1
+    assert lib.bsg_test_decode_e4m3(None, None, 0, None) == 0
+    assert lib.bsg_test_decode_e4m3(None, None, 4, None) == 1
+    assert lib.bsg_test_decode_nvfp4(None, None, None, -16, None) == 2
+    assert lib.bsg_test_decode_nvfp4(None, None, None, 24, None) == 2
+    assert lib.bsg_test_decode_nvfp4(None, None, None, 32, None) == 1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(bsg.LibraryNotBuilt):
+        import importlib
+        mod = importlib.import_module("block_scaled_precision_gemm_amd")
+        saved = mod._lib
+        try:
+            mod._lib = None
+            mod.load_library(str(tmp_path / "nope.so"))
+        finally:
+            mod._lib = saved

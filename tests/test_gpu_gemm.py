@@ -1,0 +1,201 @@
+"""GPU parity of the block-scaled GEMM against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_gemm_amd as bsg
+import seeded_inputs as si
+from gpu_util import make_plan, run, to_device
+from oracle import compare, reference
+
+pytestmark = pytest.mark.gpu
+
+# the four shapes of the nvFuser page's test_mxfp8_gemm, plus ragged / multi-tile shapes
+PAGE_SHAPES = [(128, 128, 128), (128, 128, 256), (256, 128, 128), (128, 256, 256)]
+RAGGED_SHAPES = [(1, 16, 32), (33, 48, 96), (100, 80, 160), (257, 272, 320), (130, 528, 1024)]
+
+
+def _check(p, rows=None, rel=1e-2):
+    D = run(p)
+    ref = reference(p, rows=rows)
+    if rows is not None:
+        D = D[rows]
+    rep = compare(D, ref, p["alpha"], p["silu"], p["out"], rel=rel)
+    print(f"[parity] {p['fmt']} {p['M']}x{p['N']}x{p['K']} {p['out']} max_rel={rep['max_rel_err']:.3g} "
+          f"max_err/S={rep['max_err_over_S']:.3g} by_floor={rep['n_passed_by_floor']}/{rep['n']}", flush=True)
+    assert rep["ok"], rep
+    return rep
+
+
+def _exact_regime_problem(fmt, M, N, K, seed, out):
+    """Products confined to a narrow exponent range with per-row / per-column constant scales: the
+    MFMA's internal alignment then drops no bit and every fp32 partial sum is exact, so D must equal
+    the oracle bit for bit."""
+    g = np.random.default_rng(seed)
+    if fmt == "mxfp8":  # E4M3 elements +-[1, 1.875] (exponent field 7), E8M0 scales constant along K
+        A = ((g.integers(0, 2, (M, K)) << 7) | (7 << 3) | g.integers(0, 8, (M, K))).astype(np.uint8)
+        B = ((g.integers(0, 2, (N, K)) << 7) | (7 << 3) | g.integers(0, 8, (N, K))).astype(np.uint8)
+        sA = np.repeat(g.integers(118, 136, (M, 1)), K // 32, axis=1).astype(np.uint8)
+        sB = np.repeat(g.integers(118, 136, (N, 1)), K // 32, axis=1).astype(np.uint8)
+    else:  # E2M1 elements +-{1, 1.5}, E4M3 scales constant along K
+        qa = (g.integers(0, 2, (M, K)) << 3 | g.integers(2, 4, (M, K))).astype(np.uint8)
+        qb = (g.integers(0, 2, (N, K)) << 3 | g.integers(2, 4, (N, K))).astype(np.uint8)
+        A, B = si.pack_e2m1(qa), si.pack_e2m1(qb)
+        sA = np.repeat(g.integers(0x20, 0x50, (M, 1)), K // 16, axis=1).astype(np.uint8)
+        sB = np.repeat(g.integers(0x20, 0x50, (N, 1)), K // 16, axis=1).astype(np.uint8)
+    return dict(fmt=fmt, M=M, N=N, K=K, A=A, B=B, sA=sA, sB=sB, alpha=np.float32(0.5), bias=None, silu=False,
+                out=out)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("out", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(160, 96, 1024), (33, 272, 96), (256, 256, 2048)], ids=lambda s: "x".join(map(str, s)))
+def test_exact_regime_bit_exact(fmt, out, shape):
+    p = _exact_regime_problem(fmt, *shape, seed=sum(shape), out=out)
+    D = run(p)
+    R = reference(p)["bits"]
+    assert np.array_equal(D, R), f"{int((D != R).sum())} of {D.size} entries differ"
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("out", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", PAGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_page_shapes(fmt, out, shape):
+    M, N, K = shape
+    _check(si.problem(fmt, M, N, K, seed=100 + M + N + K, out=out))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("shape", RAGGED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_shapes(fmt, shape):
+    M, N, K = shape
+    _check(si.problem(fmt, M, N, K, seed=200 + M, out="bf16", alpha=0.75))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("bias,silu", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("out", ["bf16", "f16"])
+def test_epilogue_variants(fmt, bias, silu, out):
+    _check(si.problem(fmt, 192, 160, 256, seed=300, bias=bias, silu=silu, out=out, alpha=0.5))
+
+
+def test_config_mxfp8_256():
+    _check(si.workload("mxfp8_256"))
+
+
+def test_config_mxfp8_4096_sampled_rows():
+    p = si.workload("mxfp8_4096")
+    rows = np.unique(np.concatenate([np.arange(0, 4096, 97), [4095]]))
+    _check(p, rows=rows)
+
+
+def test_config_mxfp8_8192_silu_sampled_rows():
+    p = si.workload("mxfp8_8192_silu")
+    rows = np.unique(np.concatenate([np.arange(0, 8192, 331), [8191]]))
+    _check(p, rows=rows)
+
+
+def test_config_nvfp4_128x8192x8192_full():
+    _check(si.workload("nvfp4_128x8192x8192_silu"))
+
+
+def test_config_nvfp4_256x4096x4096_all_sets():
+    plan = None
+    for s in range(3):
+        p = si.workload("nvfp4_256x4096x4096_loop", set_id=s)
+        plan = plan or make_plan(p)
+        D = run(p, plan=plan)
+        rep = compare(D, reference(p), p["alpha"], p["silu"], p["out"])
+        assert rep["ok"], (s, rep)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+def test_power_of_two_scale_bump_is_exact(fmt):
+    # raising every scale of A by 2^k multiplies each product, hence each fp32 partial sum, by 2^k
+    # exactly; so D's bits shift by k in the exponent field (no bias, no SiLU, values in range)
+    p = si.problem(fmt, 96, 64, 256, seed=400, out="bf16")
+    if fmt == "nvfp4":  # normal E4M3 scales with exponent fields 4..11, so +1 stays normal
+        g = np.random.default_rng(7)
+        p["sA"] = (g.integers(4, 12, size=p["sA"].shape) << 3 | g.integers(0, 8, size=p["sA"].shape)).astype(np.uint8)
+    D0 = run(p)
+    q = dict(p)
+    k = 3 if fmt == "mxfp8" else 1
+    q["sA"] = (p["sA"].astype(np.int64) + (3 if fmt == "mxfp8" else 8)).astype(np.uint8)
+    D1 = run(q)
+    nz = (D0 & 0x7FFF) != 0
+    assert np.array_equal(D1[nz].astype(np.int64) - D0[nz], np.full(int(nz.sum()), k << 7))
+    assert np.array_equal(D1[~nz], D0[~nz])
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+def test_permuting_b_rows_permutes_d_columns(fmt):
+    p = si.problem(fmt, 64, 128, 256, seed=500, out="f16", bias=True, silu=True)
+    D0 = run(p)
+    perm = np.random.default_rng(1).permutation(128)
+    q = dict(p, B=p["B"][perm], sB=p["sB"][perm], bias=p["bias"][perm])
+    D1 = run(q)
+    assert np.array_equal(D1, D0[:, perm])
+
+
+def test_deterministic_and_alpha_ptr_matches():
+    p = si.problem("mxfp8", 300, 256, 512, seed=600, bias=True, out="bf16", alpha=0.37)
+    plan = make_plan(p)
+    dev = to_device(p)
+    D0 = run(p, plan=plan, dev=dev)
+    D1 = run(p, plan=plan, dev=dev)
+    assert np.array_equal(D0, D1)
+    alpha_dev = torch.tensor([float(p["alpha"])], dtype=torch.float32, device="cuda")
+    dev["D"].zero_()
+    plan.run_alpha_ptr(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha_dev, bias=dev["bias"])
+    torch.cuda.synchronize()
+    assert np.array_equal(dev["D"].cpu().numpy().view(np.uint16), D0)
+
+
+def test_e8m0_extreme_scales():
+    # one nonzero product per row: A[i, 0] = B[j, 0] = 1.0, sA[i, 0] sweeps codes 1..254, sB = 127
+    M, N, K = 254, 16, 32
+    A = np.zeros((M, K), np.uint8)
+    A[:, 0] = 0x38
+    B = np.zeros((N, K), np.uint8)
+    B[:, 0] = 0x38
+    sA = np.arange(1, 255, dtype=np.uint8)[:, None]
+    sB = np.full((N, 1), 127, np.uint8)
+    p = dict(fmt="mxfp8", M=M, N=N, K=K, A=A, B=B, sA=sA, sB=sB, alpha=np.float32(1), bias=None, silu=False,
+             out="bf16")
+    D = run(p)
+    assert np.array_equal(D, reference(p)["bits"])
+
+
+def test_errors_reported_without_launch():
+    p = si.problem("mxfp8", 64, 64, 64, seed=700)
+    plan = make_plan(p)
+    dev = to_device(p)
+    with pytest.raises(bsg.BsgError) as e:
+        plan.run(dev["A"].data_ptr() + 1, dev["B"], dev["sA"], dev["sB"], dev["D"])
+    assert e.value.status_name == "BSG_ERR_ALIGN"
+    with pytest.raises(bsg.BsgError) as e:
+        plan.run(0, dev["B"], dev["sA"], dev["sB"], dev["D"])
+    assert e.value.status_name == "BSG_ERR_NULL"
+    pb = bsg.Plan("mxfp8", 64, 64, 64, bias=True)
+    with pytest.raises(bsg.BsgError) as e:
+        pb.run(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], bias=None)
+    assert e.value.status_name == "BSG_ERR_NULL"
+
+
+def test_no_device_allocation_per_call():
+    p = si.workload("nvfp4_256x4096x4096_loop")
+    plan = make_plan(p)
+    dev = to_device(p)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(1000):
+        plan.run(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha=float(p["alpha"]))
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
+
+
+def test_plan_info():
+    plan = bsg.Plan("mxfp8", 4096, 4096, 4096, out="bf16")
+    info = plan.info()
+    assert info["workspace_bytes"] == 0 and info["block"] > 0 and info["variant"].startswith("mxfp8")
