@@ -41,12 +41,23 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t nib) {
 
 namespace bsg {
 
-// Eight E2M1 codes of one dword (nibble j = element j), each times `scale`, as bf16x8.  The fp32
-// product is exact (<= 6 significant bits) and so is its conversion to bf16.
-__device__ __forceinline__ v8bf e2m1x8_scaled_bf16(uint32_t packed, float scale) {
-  v8bf r;
+// Two fp32 values that are exactly representable in bf16 -> one dword of two bf16 (low half = lo).
+__device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
+  // exact inputs: dropping the low 16 bits of each fp32 is the value itself
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// Eight E2M1 codes of one dword (nibble j = element j), each times `scale`, as four dwords of
+// bf16 pairs (dword i holds elements 2i, 2i+1).  The fp32 product is exact (<= 6 significant
+// bits), hence so is the bf16 value.
+__device__ __forceinline__ v4i e2m1x8_scaled_bf16x8(uint32_t packed, float scale) {
+  v4i r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (__bf16)(e2m1_to_f32(packed >> (4 * j)) * scale);
+  for (int i = 0; i < 4; ++i) {
+    const float lo = e2m1_to_f32(packed >> (8 * i)) * scale;
+    const float hi = e2m1_to_f32(packed >> (8 * i + 4)) * scale;
+    r[i] = (int)pack_bf16x2_exact(lo, hi);
+  }
   return r;
 }
 

@@ -20,9 +20,8 @@ __global__ void decode_e4m3_kernel(const uint8_t* codes, float* out, int64_t n) 
 __global__ void decode_nvfp4_kernel(const uint32_t* packed, const uint8_t* scales, uint16_t* out, int64_t n_words) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n_words) return;
-  const bsg::v8bf v = bsg::e2m1x8_scaled_bf16(packed[t], bsg::e4m3_to_f32(scales[t >> 1]));
-#pragma unroll
-  for (int j = 0; j < 8; ++j) out[8 * t + j] = __builtin_bit_cast(uint16_t, v[j]);
+  const bsg::v4i v = bsg::e2m1x8_scaled_bf16x8(packed[t], bsg::e4m3_to_f32(scales[t >> 1]));
+  ((bsg::v4i*)out)[t] = v;
 }
 
 bsg_status launch_status(hipError_t e) {

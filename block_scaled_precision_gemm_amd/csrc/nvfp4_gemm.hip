@@ -60,9 +60,9 @@ __global__ __launch_bounds__(256) void nvfp4_direct_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const v8bf a = e2m1x8_scaled_bf16((uint32_t)qa[t], t < 2 ? sa0 : sa1);
-      const v8bf b = e2m1x8_scaled_bf16((uint32_t)qb[t], t < 2 ? sb0 : sb1);
-      acc = mfma_bf16_32x32x16(a, b, acc);
+      const v4i a = e2m1x8_scaled_bf16x8((uint32_t)qa[t], t < 2 ? sa0 : sa1);
+      const v4i b = e2m1x8_scaled_bf16x8((uint32_t)qb[t], t < 2 ? sb0 : sb1);
+      acc = mfma_bf16_32x32x16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), acc);
     }
   }
   const int n = n0 + r;

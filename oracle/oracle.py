@@ -92,6 +92,11 @@ def unpack_e2m1(packed: np.ndarray, K: int) -> np.ndarray:
 # Dequantisation: value = element * scale of the block holding k
 # --------------------------------------------------------------------------
 
+def _decode_by_table(decode, codes, n_codes: int) -> np.ndarray:
+    """decode(codes) for a large code array: decode each of the n_codes possible codes once, then index."""
+    return decode(np.arange(n_codes))[np.asarray(codes, dtype=np.uint8)]
+
+
 def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """[R, K] E4M3 codes, [R, K/32] E8M0 codes -> exact fp64 [R, K].
 
@@ -99,7 +104,9 @@ def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """
     R, K = codes.shape
     assert scales.shape == (R, K // MX_BLOCK)
-    return decode_e4m3(codes) * np.repeat(decode_e8m0(scales), MX_BLOCK, axis=1)
+    out = _decode_by_table(decode_e4m3, codes, 256)
+    out *= np.repeat(_decode_by_table(decode_e8m0, scales, 256), MX_BLOCK, axis=1)
+    return out
 
 
 def dequant_nvfp4(packed: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
@@ -110,7 +117,9 @@ def dequant_nvfp4(packed: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
     """
     R = packed.shape[0]
     assert packed.shape == (R, K // 2) and scales.shape == (R, K // NV_BLOCK)
-    return decode_e2m1(unpack_e2m1(packed, K)) * np.repeat(decode_e4m3(scales), NV_BLOCK, axis=1)
+    out = _decode_by_table(decode_e2m1, unpack_e2m1(packed, K), 16)
+    out *= np.repeat(_decode_by_table(decode_e4m3, scales, 256), NV_BLOCK, axis=1)
+    return out
 
 
 def dequant(fmt: str, data: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
