@@ -209,7 +209,8 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   a.K = (int)problem->K;
   a.tiles_m = (int)((problem->M + v.tile_m - 1) / v.tile_m);
   a.tiles_n = (int)((problem->N + v.tile_n - 1) / v.tile_n);
-  plan->grid = dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, 1);
+  plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n), 1, 1)
+                             : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, 1);
   plan->block = dim3((unsigned)v.block_threads, 1, 1);
   *out_plan = plan;
   return BSG_OK;
@@ -225,8 +226,9 @@ static inline bsg_status run_impl(bsg_plan plan, const void* A, const void* B, c
     set_error("null operand pointer (A=%p B=%p sA=%p sB=%p D=%p bias=%p)", A, B, sA, sB, D, (const void*)bias);
     return BSG_ERR_NULL;
   }
-  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D) & 15u) {
-    set_error("A, B and D must be 16-byte aligned (A=%p B=%p D=%p)", A, B, D);
+  if ((((uintptr_t)A | (uintptr_t)B | (uintptr_t)D) & 15u) || (((uintptr_t)sA | (uintptr_t)sB) & 3u)) {
+    set_error("A, B and D must be 16-byte aligned and sA, sB 4-byte aligned (A=%p B=%p D=%p sA=%p sB=%p)", A, B,
+              D, sA, sB);
     return BSG_ERR_ALIGN;
   }
   bsg::GemmArgs a = plan->args;
@@ -238,7 +240,7 @@ static inline bsg_status run_impl(bsg_plan plan, const void* A, const void* B, c
   a.alpha = alpha;
   a.alpha_ptr = alpha_dev;
   a.D = D;
-  const hipError_t e = plan->launch(a, plan->grid, plan->block, plan->lds_bytes, (hipStream_t)stream);
+  const hipError_t e = plan->launch(a, plan->grid, plan->block, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("kernel launch failed: %s", hipGetErrorString(e));
     return BSG_ERR_HIP;

@@ -32,20 +32,23 @@ struct GemmArgs {
   int tiles_m, tiles_n;   // output tile grid
 };
 
-// A launcher: enqueues one kernel on `stream` with a precomputed launch shape.
-typedef hipError_t (*LaunchFn)(const GemmArgs& args, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream);
+// A launcher: enqueues one kernel on `stream` with a precomputed launch shape.  Kernels use static
+// LDS only; no dynamic LDS is requested at launch.
+typedef hipError_t (*LaunchFn)(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream);
 
 struct KernelVariant {
   const char* name;
   LaunchFn launch;
   int tile_m, tile_n, tile_k;
   int block_threads;
-  uint32_t lds_bytes;
+  uint32_t lds_bytes;    // static LDS of the kernel (informational)
+  bool linear_grid;      // grid = (tiles_m * tiles_n) workgroups in x; else (tiles_n, tiles_m)
 };
 
 // Variant tables, one per format: index = out dtype (0 bf16, 1 f16) * 4 + bias * 2 + silu.
 // Each kernel family returns its table for the M bucket it serves.
 const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K);
+const KernelVariant* mxfp8_tiled_variants();
 const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K);
 
 inline int variant_index(Out out, bool bias, bool silu) {

@@ -80,13 +80,13 @@ __global__ __launch_bounds__(256) void mxfp8_direct_kernel(GemmArgs p) {
 }
 
 template <Out O, bool BIAS, bool SILU>
-hipError_t launch_direct(const GemmArgs& args, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream) {
+hipError_t launch_direct(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
-  return hipLaunchKernel((const void*)&mxfp8_direct_kernel<O, BIAS, SILU>, grid, block, kargs, lds, stream);
+  return hipLaunchKernel((const void*)&mxfp8_direct_kernel<O, BIAS, SILU>, grid, block, kargs, 0, stream);
 }
 
 #define BSG_MX_DIRECT(O, B, S) \
-  { "mxfp8_direct_64x64", &launch_direct<O, B, S>, 64, 64, 64, 256, 0 }
+  { "mxfp8_direct_64x64", &launch_direct<O, B, S>, 64, 64, 64, 256, 0, false }
 const KernelVariant kDirect[8] = {
     BSG_MX_DIRECT(Out::BF16, false, false), BSG_MX_DIRECT(Out::BF16, false, true),
     BSG_MX_DIRECT(Out::BF16, true, false),  BSG_MX_DIRECT(Out::BF16, true, true),
@@ -97,6 +97,9 @@ const KernelVariant kDirect[8] = {
 
 }  // namespace
 
-const KernelVariant* mxfp8_variants(int64_t /*M*/, int64_t /*N*/, int64_t /*K*/) { return kDirect; }
+// K % 128 == 0 (every configured workload) takes the LDS-tiled kernel; other K use the direct one.
+const KernelVariant* mxfp8_variants(int64_t /*M*/, int64_t /*N*/, int64_t K) {
+  return K % 128 == 0 ? mxfp8_tiled_variants() : kDirect;
+}
 
 }  // namespace bsg

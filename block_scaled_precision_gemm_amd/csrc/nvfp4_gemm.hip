@@ -78,13 +78,13 @@ __global__ __launch_bounds__(256) void nvfp4_direct_kernel(GemmArgs p) {
 }
 
 template <Out O, bool BIAS, bool SILU>
-hipError_t launch_direct(const GemmArgs& args, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream) {
+hipError_t launch_direct(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
-  return hipLaunchKernel((const void*)&nvfp4_direct_kernel<O, BIAS, SILU>, grid, block, kargs, lds, stream);
+  return hipLaunchKernel((const void*)&nvfp4_direct_kernel<O, BIAS, SILU>, grid, block, kargs, 0, stream);
 }
 
 #define BSG_NV_DIRECT(O, B, S) \
-  { "nvfp4_direct_64x64", &launch_direct<O, B, S>, 64, 64, 64, 256, 0 }
+  { "nvfp4_direct_64x64", &launch_direct<O, B, S>, 64, 64, 64, 256, 0, false }
 const KernelVariant kDirect[8] = {
     BSG_NV_DIRECT(Out::BF16, false, false), BSG_NV_DIRECT(Out::BF16, false, true),
     BSG_NV_DIRECT(Out::BF16, true, false),  BSG_NV_DIRECT(Out::BF16, true, true),

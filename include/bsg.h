@@ -112,7 +112,7 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan);
 
 /* Enqueue D = epi(alpha * A x B^T (+ bias)) on `stream` (a hipStream_t; NULL = the null stream).
  * A, B, sA, sB, D: device pointers laid out as described at the top of this file; A, B and D must be
- * 16-byte aligned.  bias: device float[N], required iff the plan has BSG_EPI_BIAS (ignored otherwise).
+ * 16-byte aligned, sA and sB 4-byte aligned.  bias: device float[N], required iff the plan has BSG_EPI_BIAS (ignored otherwise).
  * alpha: host fp32 value.  Returns after enqueueing (asynchronous).  Errors: BSG_ERR_NULL,
  * BSG_ERR_ALIGN, BSG_ERR_HIP (launch failure). */
 bsg_status bsg_run(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB,
