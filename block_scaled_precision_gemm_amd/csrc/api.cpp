@@ -15,7 +15,7 @@
 #include <mutex>
 #include <new>
 
-#include "../../include/bsg.h"
+#include "bsg.h"
 #include "common.h"
 
 namespace bsg {

@@ -5,7 +5,7 @@
 #include <chrono>
 #include <vector>
 
-#include "../../include/bsg_bench.h"
+#include "bsg_bench.h"
 
 namespace bsg {
 void set_error(const char* fmt, ...);

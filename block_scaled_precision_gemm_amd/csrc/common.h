@@ -48,7 +48,8 @@ struct KernelVariant {
 // Variant tables, one per format: index = out dtype (0 bf16, 1 f16) * 4 + bias * 2 + silu.
 // Each kernel family returns its table for the M bucket it serves.
 const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K);
-const KernelVariant* mxfp8_tiled_variants();
+const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N);
+const KernelVariant* mxfp8_pipe_variants();
 const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K);
 
 inline int variant_index(Out out, bool bias, bool silu) {

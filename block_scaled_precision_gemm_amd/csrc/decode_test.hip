@@ -1,6 +1,6 @@
 // Element-wise launchers of the device decoders (codec.h), for bit-exact tests against a CPU
 // decoding of every code.  Not on the GEMM path; they run the very functions the GEMM kernels use.
-#include "../../include/bsg_testing.h"
+#include "bsg_testing.h"
 #include "codec.h"
 #include "common.h"
 

@@ -1,14 +1,15 @@
-// MXFP8 block-scaled GEMM, LDS-tiled kernel for gfx950 (the main path for K % 128 == 0).
+// MXFP8 block-scaled GEMM, LDS-tiled kernels for gfx950 (the path for K % 128 == 0).
 //
 // Same operation as mxfp8_gemm.hip (E4M3 operands with one E8M0 scale per 32 K elements, the
 // mx_float8_t / float_ue8m0_t operands of the nvFuser PR #5736 page), organised for CDNA4:
 //
-// * Workgroup tile 256 x 256, K tile 128, 4 waves in a 2 x 2 arrangement, each wave owning a
-//   128 x 128 block of D as 4 x 4 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4 (256 fp32
-//   accumulator registers per lane).
-// * A and B K-tiles are copied global -> LDS with global_load_lds_dwordx4 (16 bytes per lane, no
-//   register staging) into a two-stage ring (2 x 64 KiB), so the copy of tile k+1 runs while the
-//   MFMAs consume tile k; one workgroup barrier per K tile.
+// * Workgroup tile BM x BN, K tile 128, WM x WN waves, each wave owning a (BM/WM) x (BN/WN) block
+//   of D as 32 x 32 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4.  With 8 waves two waves
+//   share each SIMD, so one wave's LDS reads overlap the other's MFMAs.
+// * A and B K-tiles are copied global -> LDS with buffer_load_dwordx4 ... lds (16 bytes per lane,
+//   no register staging) into a two-stage ring, so the copy of tile k+1 runs while the MFMAs consume
+//   tile k; one workgroup barrier per K tile.  Each lane's buffer offsets are computed once; the K
+//   position is a scalar offset.  Rows past M (or N) lie outside the buffer range and read as 0.
 // * LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row R is stored at chunk
 //   c ^ f(R), f(R) = (R & 7) ^ ((R >> 3) & 1).  The MFMA fragment reads (ds_read_b128 of one
 //   chunk from 8 or 16 consecutive rows) then hit distinct banks.
@@ -25,15 +26,26 @@
 #include "epilogue.h"
 
 namespace bsg {
-namespace {
+// Named (not anonymous) namespace: kernel templates instantiated on these configuration types need
+// external linkage for their host-side launch stubs to be emitted.
+namespace mxt {
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int A_TILE = BM * BK;            // bytes per stage
-constexpr int B_TILE = BN * BK;
-constexpr int STAGE = A_TILE + B_TILE;     // 64 KiB
-constexpr int THREADS = 256;
+constexpr int BK = 128;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
+  static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
+  static constexpr int A_TILE = BM * BK, B_TILE = BN * BK, STAGE = A_TILE + B_TILE;
+  static constexpr int A_COPIES = BM / 8 / WAVES, B_COPIES = BN / 8 / WAVES;  // per wave per K tile
+  static_assert(TM >= 1 && TN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
+  static_assert(A_COPIES * 8 * WAVES == BM && B_COPIES * 8 * WAVES == BN, "copy split");
+  static_assert(2 * STAGE <= 160 * 1024, "LDS");
+};
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -54,34 +66,56 @@ __device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
   return make_int2(first_m + in_group % gsize, in_group / gsize);
 }
 
-// Copy one 256 x 128-byte operand tile (rows row0.., K bytes k0..k0+127) into LDS `dst`.
-// Wave w issues 8 instructions; instruction q fills LDS rows 8*(8w+q) .. +8 (1 KiB).  Lane j of
-// an instruction writes LDS bytes [16j, 16j+16) of that KiB: row R = 8*(8w+q) + j/8, physical chunk
-// j%8, which holds logical chunk (j%8) ^ swz(R).
-__device__ __forceinline__ void copy_tile(const uint8_t* __restrict__ src, int ld, int row0, int rows_valid, int k0,
-                                          uint8_t* dst, int wave, int lane) {
+// Copy plan for one operand tile (ROWS rows x 128 bytes): wave w issues COPIES instructions; its
+// instruction q fills LDS rows 8*(COPIES*w + q) .. +8 (1 KiB).  Lane j of an instruction writes LDS
+// bytes [16j, 16j+16) of that KiB: row R = 8*(COPIES*w+q) + j/8, physical chunk j%8, which holds
+// logical chunk (j%8) ^ swz(R).  voff[q] is the lane's byte offset of that chunk in the operand
+// buffer (relative to the tile's first row, at K position 0).
+template <int COPIES>
+struct CopyPlan {
+  uint32_t voff[COPIES];
+  int lds_row0;  // first LDS row of the wave's first instruction (wave-uniform)
+
+  __device__ __forceinline__ void init(int wave, int lane, int ld) {
+    lds_row0 = 8 * COPIES * wave;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int R0 = 8 * (8 * wave + q);
-    const int R = R0 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(R);
-    const int grow = min(R, rows_valid - 1);  // rows past the edge re-read a valid row; never stored
-    const uint8_t* g = src + (size_t)(row0 + grow) * ld + k0 + 16 * c;
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(dst + R0 * BK), 16, 0, 0);
+    for (int q = 0; q < COPIES; ++q) {
+      const int R = lds_row0 + 8 * q + (lane >> 3);
+      voff[q] = (uint32_t)R * (uint32_t)ld + 16u * (uint32_t)((lane & 7) ^ swz(R));
+    }
   }
-}
 
-template <Out O, bool BIAS, bool SILU>
-__global__ __launch_bounds__(THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, uint32_t k0, uint8_t* tile) const {
+#pragma unroll
+    for (int q = 0; q < COPIES; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (lds_row0 + 8 * q) * BK), 16, voff[q], k0,
+                                               0, 0);
+  }
+};
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <class C, Out O, bool BIAS, bool SILU>
+__global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+  constexpr int TM = C::TM, TN = C::TN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31, h = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int2 t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n);
-  const int m0 = t.x * BM, n0 = t.y * BN;
+  const int m0 = t.x * C::BM, n0 = t.y * C::BN;
   const int K = p.K, KB = K >> 5, KT = K / BK;
-  const int m_valid = min(BM, p.M - m0), n_valid = min(BN, p.N - n0);
+  const int m_valid = min(C::BM, p.M - m0), n_valid = min(C::BN, p.N - n0);
+
+  // operand buffers start at the tile's first row and end at the last valid row
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (size_t)m0 * K), (short)0, m_valid * K, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (size_t)n0 * K), (short)0, n_valid * K, kRsrcWord3);
+  CopyPlan<C::A_COPIES> cpA;
+  CopyPlan<C::B_COPIES> cpB;
+  cpA.init(wave, lane, K);
+  cpB.init(wave, lane, K);
 
   // per-lane LDS offsets of the two 16-byte chunks of k-step ks (see the layout comment above)
   const int f = swz(r);
@@ -91,76 +125,75 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
     off[ks][0] = 16 * ((4 * ks + h) ^ f);
     off[ks][1] = 16 * ((4 * ks + 2 + h) ^ f);
   }
-  const int a_row = (wm * 128 + r) * BK;  // LDS byte offset of this lane's row in row-tile 0
-  const int b_row = (wn * 128 + r) * BK;
+  const int a_row = (wm * TM * 32 + r) * BK;  // LDS byte offset of this lane's row in row-tile 0
+  const int b_row = (wn * TN * 32 + r) * BK;
 
-  // scale pointers: one dword = the 4 E8M0 codes of a K tile, per row-tile
-  const uint32_t* sa_ptr[4];
-  const uint32_t* sb_ptr[4];
+  // scale pointers: one dword = the 4 E8M0 codes of a K tile; rows past the edge re-read a valid row
+  const uint32_t* sa_ptr[TM];
+  const uint32_t* sb_ptr[TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int am = min(wm * 128 + 32 * i + r, m_valid - 1);
-    const int bn = min(wn * 128 + 32 * i + r, n_valid - 1);
-    sa_ptr[i] = (const uint32_t*)(p.sA + (size_t)(m0 + am) * KB);
-    sb_ptr[i] = (const uint32_t*)(p.sB + (size_t)(n0 + bn) * KB);
-  }
+  for (int i = 0; i < TM; ++i)
+    sa_ptr[i] = (const uint32_t*)(p.sA + (size_t)(m0 + min(wm * TM * 32 + 32 * i + r, m_valid - 1)) * KB);
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    sb_ptr[j] = (const uint32_t*)(p.sB + (size_t)(n0 + min(wn * TN * 32 + 32 * j + r, n_valid - 1)) * KB);
 
-  v16f acc[4][4];
+  v16f acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
+    for (int j = 0; j < TN; ++j) acc[i][j] = (v16f){};
 
   // prologue: tile 0 -> stage 0, scales of tile 0 -> registers
-  copy_tile(p.A, K, m0, m_valid, 0, lds, wave, lane);
-  copy_tile(p.B, K, n0, n_valid, 0, lds + A_TILE, wave, lane);
-  uint32_t sa_next[4], sb_next[4];
+  cpA.issue(rsA, 0, lds);
+  cpB.issue(rsB, 0, lds + C::A_TILE);
+  uint32_t sa_next[TM], sb_next[TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sa_next[i] = sa_ptr[i][0];
-    sb_next[i] = sb_ptr[i][0];
-  }
+  for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][0];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][0];
 
   for (int kt = 0; kt < KT; ++kt) {
-    uint32_t sa_cur[4], sb_cur[4];
+    uint32_t sa_cur[TM], sb_cur[TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa_cur[i] = sa_next[i];
-      sb_cur[i] = sb_next[i];
-    }
+    for (int i = 0; i < TM; ++i) sa_cur[i] = sa_next[i];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
     __syncthreads();  // tile kt is in LDS stage kt&1; everyone is done reading stage (kt+1)&1
     if (kt + 1 < KT) {
-      uint8_t* nxt = lds + ((kt + 1) & 1) * STAGE;
-      copy_tile(p.A, K, m0, m_valid, (kt + 1) * BK, nxt, wave, lane);
-      copy_tile(p.B, K, n0, n_valid, (kt + 1) * BK, nxt + A_TILE, wave, lane);
+      uint8_t* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+      const uint32_t k1 = (uint32_t)(kt + 1) * BK;
+      cpA.issue(rsA, k1, nxt);
+      cpB.issue(rsB, k1, nxt + C::A_TILE);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa_next[i] = sa_ptr[i][kt + 1];
-        sb_next[i] = sb_ptr[i][kt + 1];
-      }
+      for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][kt + 1];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][kt + 1];
     }
-    const uint8_t* sa_lds = lds + (kt & 1) * STAGE;
-    const uint8_t* sb_lds = sa_lds + A_TILE;
+    const uint8_t* a_lds = lds + (kt & 1) * C::STAGE;
+    const uint8_t* b_lds = a_lds + C::A_TILE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      v8i af[4], bf[4];
-      int sa[4], sb[4];
+      v8i af[TM], bf[TN];
+      int sa[TM], sb[TN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint8_t* pa = sa_lds + a_row + i * 32 * BK;
-        const uint8_t* pb = sb_lds + b_row + i * 32 * BK;
-        const v4i a0 = *(const v4i*)(pa + off[ks][0]), a1 = *(const v4i*)(pa + off[ks][1]);
-        const v4i b0 = *(const v4i*)(pb + off[ks][0]), b1 = *(const v4i*)(pb + off[ks][1]);
-        af[i] = (v8i){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        bf[i] = (v8i){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        // block 2*ks + h of this K tile, moved to byte 0
-        sa[i] = (int)(sa_cur[i] >> (8 * (2 * ks + h)));
-        sb[i] = (int)(sb_cur[i] >> (8 * (2 * ks + h)));
+      for (int i = 0; i < TM; ++i) {
+        const uint8_t* pa = a_lds + a_row + i * 32 * BK;
+        const v4i x0 = *(const v4i*)(pa + off[ks][0]), x1 = *(const v4i*)(pa + off[ks][1]);
+        af[i] = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        sa[i] = (int)(sa_cur[i] >> (8 * (2 * ks + h)));  // block 2*ks + h of this K tile, in byte 0
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* pb = b_lds + b_row + j * 32 * BK;
+        const v4i x0 = *(const v4i*)(pb + off[ks][0]), x1 = *(const v4i*)(pb + off[ks][1]);
+        bf[j] = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        sb[j] = (int)(sb_cur[j] >> (8 * (2 * ks + h)));
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mx(af[i], bf[j], acc[i][j], sa[i], sb[j]);
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(af[i], bf[j], acc[i][j], sa[i], sb[j]);
     }
   }
 
@@ -168,39 +201,66 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
   const float alpha = load_alpha(p);
   uint16_t* D = (uint16_t*)p.D;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 128 + 32 * j + r;
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + wn * TN * 32 + 32 * j + r;
     if (n >= p.N) continue;
     const float bv = BIAS ? p.bias[n] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        const int m = m0 + wm * TM * 32 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
         if (m < p.M) D[(size_t)m * p.N + n] = to_out_bits<O>(epi_value<SILU>(acc[i][j][e], alpha, bv));
       }
     }
   }
 }
 
-template <Out O, bool BIAS, bool SILU>
+template <class C, Out O, bool BIAS, bool SILU>
 hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
-  return hipLaunchKernel((const void*)&mxfp8_tiled_kernel<O, BIAS, SILU>, grid, block, kargs, 0, stream);
+  return hipLaunchKernel((const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU>, grid, block, kargs, 0, stream);
 }
 
-#define BSG_MX_TILED(O, B, S) \
-  { "mxfp8_tiled_256x256x128", &launch_tiled<O, B, S>, BM, BN, BK, THREADS, 2 * STAGE, true }
-const KernelVariant kTiled[8] = {
-    BSG_MX_TILED(Out::BF16, false, false), BSG_MX_TILED(Out::BF16, false, true),
-    BSG_MX_TILED(Out::BF16, true, false),  BSG_MX_TILED(Out::BF16, true, true),
-    BSG_MX_TILED(Out::F16, false, false),  BSG_MX_TILED(Out::F16, false, true),
-    BSG_MX_TILED(Out::F16, true, false),   BSG_MX_TILED(Out::F16, true, true),
-};
+#define BSG_MX_TILED(NAME, C, O, B, S) \
+  { NAME, &launch_tiled<C, O, B, S>, C::BM, C::BN, BK, C::THREADS, 2 * C::STAGE, true }
+#define BSG_MX_TABLE(NAME, C)                                                                    \
+  {                                                                                              \
+    BSG_MX_TILED(NAME, C, Out::BF16, false, false), BSG_MX_TILED(NAME, C, Out::BF16, false, true), \
+    BSG_MX_TILED(NAME, C, Out::BF16, true, false), BSG_MX_TILED(NAME, C, Out::BF16, true, true),   \
+    BSG_MX_TILED(NAME, C, Out::F16, false, false), BSG_MX_TILED(NAME, C, Out::F16, false, true),   \
+    BSG_MX_TILED(NAME, C, Out::F16, true, false), BSG_MX_TILED(NAME, C, Out::F16, true, true)      \
+  }
+
+using Large = Cfg<256, 256, 2, 4>;  // 8 waves of 128 x 64
+using Small = Cfg<128, 128, 2, 2>;  // 4 waves of 64 x 64, for problems with few large tiles
+
+// Explicit instantiations: taking a kernel template's address only inside another template does not
+// make the compiler emit its host-side launch stub when the template argument is a class type.
+#define BSG_MX_INST(C)                                                            \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, false>(GemmArgs); \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, true>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, false>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, true>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, false>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, true>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, false>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, true>(GemmArgs);
+BSG_MX_INST(Large)
+BSG_MX_INST(Small)
+#undef BSG_MX_INST
+
+const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);
+const KernelVariant kSmall[8] = BSG_MX_TABLE("mxfp8_tiled_128x128x128_w4", Small);
+#undef BSG_MX_TABLE
 #undef BSG_MX_TILED
 
-}  // namespace
+}  // namespace mxt
 
-const KernelVariant* mxfp8_tiled_variants() { return kTiled; }
+// Large tiles once they give at least one workgroup per CU (256 CUs); smaller tiles otherwise.
+const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N) {
+  const int64_t large_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return large_tiles >= 256 ? mxt::kLarge : mxt::kSmall;
+}
 
 }  // namespace bsg
