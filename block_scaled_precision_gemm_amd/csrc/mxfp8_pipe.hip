@@ -38,7 +38,10 @@ constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 4 x 2 MFMA tiles per wav
 constexpr int A_TILE = BM * BK, B_TILE = BN * BK, STAGE = A_TILE + B_TILE;  // 32 KiB
 constexpr int SCALE_BYTES = 16;                                            // per row per 8 K tiles
 constexpr int SCALE_A = BM * SCALE_BYTES, SCALE_B = BN * SCALE_BYTES;      // 4 KiB each
-constexpr int LDS_BYTES = NS * STAGE + SCALE_A + SCALE_B;                  // 136 KiB
+constexpr int MAIN_LDS = NS * STAGE + SCALE_A + SCALE_B;                   // 136 KiB
+// epilogue staging: each wave's 128 x 64 output block, rows padded to 144 bytes (16-byte aligned)
+constexpr int EPI_ROW = 144, EPI_WAVE = 128 * EPI_ROW;
+constexpr int LDS_BYTES = MAIN_LDS > WAVES * EPI_WAVE ? MAIN_LDS : WAVES * EPI_WAVE;  // 144 KiB
 constexpr int COPIES = (BM + BN) / 16 / WAVES;  // 16-row copy instructions per wave per tile: 4
 constexpr uint32_t kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data format (gfx9 family)
 static_assert(COPIES == 4, "copy split");
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pipe_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(af[i], bf[j], acc[i][j], ssa[i], ssb[j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(bf[j], af[i], acc[i][j], ssb[j], ssa[i]);
   };
   for (; kb < KT; kb += UNROLL) {
     step(std::integral_constant<int, 0>{});
@@ -226,23 +229,47 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pipe_kernel(GemmArgs p) {
     step(std::integral_constant<int, 6>{});
     step(std::integral_constant<int, 7>{});
   }
-  wait_vmcnt<0>();  // no LDS-DMA write may outlive the workgroup
-
+  // Epilogue.  acc[i][j] holds the 32 x 32 block (rows 32i.., columns 32j.. of the wave's 128 x 64)
+  // transposed: lane (r, h), element 4g + c is row r, column 8g + 4h + c.  Each lane applies alpha,
+  // bias and SiLU to its values, converts them, writes 4-column pieces into the wave's LDS block, and
+  // the wave then stores its block row by row with 16 bytes per lane (128-byte row segments).
+  wait_vmcnt_barrier<0>();  // no LDS-DMA write in flight, every wave done with the pipeline buffers
   const float alpha = load_alpha(p);
-  uint16_t* D = (uint16_t*)p.D;
+  uint8_t* const eb = lds + wave * EPI_WAVE;
+  const int nw = n0 + wn * TN * 32;  // first column of the wave's block
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int n = n0 + wn * TN * 32 + 32 * j + r;
-    if (n >= p.N) continue;
-    const float bv = BIAS ? p.bias[n] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int g = 0; g < 4; ++g) {
+      const int c0 = 32 * j + 8 * g + 4 * h;  // first of this lane's 4 columns in the block
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BIAS) {
+        if (nw + c0 < p.N) {
+          const v4f b4 = *(const v4f*)(p.bias + nw + c0);
+          bv[0] = b4[0]; bv[1] = b4[1]; bv[2] = b4[2]; bv[3] = b4[3];
+        }
+      }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * TM * 32 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m < p.M) D[(size_t)m * p.N + n] = to_out_bits<O>(epi_value<SILU>(acc[i][j][e], alpha, bv));
+      for (int i = 0; i < TM; ++i) {
+        const v16f& a = acc[i][j];
+        const uint32_t lo = pack2_out<O>(epi_value<SILU>(a[4 * g + 0], alpha, bv[0]),
+                                         epi_value<SILU>(a[4 * g + 1], alpha, bv[1]));
+        const uint32_t hi = pack2_out<O>(epi_value<SILU>(a[4 * g + 2], alpha, bv[2]),
+                                         epi_value<SILU>(a[4 * g + 3], alpha, bv[3]));
+        *(uint2*)(eb + (32 * i + r) * EPI_ROW + 2 * c0) = make_uint2(lo, hi);
       }
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (block is wave-private)
+  uint16_t* D = (uint16_t*)p.D;
+  const int mw = m0 + wm * TM * 32;  // first row of the wave's block
+  const int cc = 8 * (lane & 7);     // this lane's 8 columns
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int row = 8 * q + (lane >> 3);
+    const v4i v = *(const v4i*)(eb + row * EPI_ROW + 2 * cc);
+    const int m = mw + row, n = nw + cc;
+    if (m < p.M && n < p.N) *(v4i*)(D + (size_t)m * p.N + n) = v;
   }
 }
 
