@@ -97,12 +97,12 @@ const KernelVariant kDirect[8] = {
 
 }  // namespace
 
-// Kernel choice by shape: the deep-pipelined kernel for K % 512 == 0 once 256 x 256 tiles give at
+// Kernel choice by shape: the 4-wave pipelined kernel for K % 512 == 0 once 256 x 256 tiles give at
 // least one workgroup per CU; the two-stage tiled kernels for other K % 128 == 0; the direct kernel
 // for the remaining K % 32 == 0.
 const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K) {
   const int64_t large_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (K % 512 == 0 && large_tiles >= 256) return mxfp8_pipe_variants();
+  if (K % 512 == 0 && large_tiles >= 256) return mxfp8_plr_variants();
   return K % 128 == 0 ? mxfp8_tiled_variants(M, N) : kDirect;
 }
 
