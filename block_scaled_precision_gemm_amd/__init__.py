@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_e4m3", "decode_nvfp4",
+__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_e4m3", "decode_nvfp4", "decode_nvfp4_f16",
            "FORMATS", "OUT_DTYPES", "abi_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +64,7 @@ _SIGNATURES = {
     "bsg_abi_version": (ctypes.c_int, []),
     "bsg_test_decode_e4m3": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP]),
     "bsg_test_decode_nvfp4": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int64, _VP]),
+    "bsg_test_decode_nvfp4_f16": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int64, _VP]),
     "bsg_bench_loop": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_VP), ctypes.c_int,
@@ -199,3 +200,10 @@ def decode_nvfp4(packed, scale_codes, out_bf16, n_elements: int, stream=None) ->
     """out_bf16[k] = device dequantisation of NVFP4 element k (packed[k/2] nibble, scale_codes[k/16])."""
     _check(load_library().bsg_test_decode_nvfp4(_ptr(packed), _ptr(scale_codes), _ptr(out_bf16), n_elements,
                                                 _stream(stream)))
+
+
+def decode_nvfp4_f16(packed, scale_codes, out_f16, n_elements: int, stream=None) -> None:
+    """out_f16[k] = device fp16 dequantisation of NVFP4 element k times 2^-7, through the tiled
+    kernels' routine (packed[k/2] nibble, scale_codes[k/16]); n_elements a multiple of 32."""
+    _check(load_library().bsg_test_decode_nvfp4_f16(_ptr(packed), _ptr(scale_codes), _ptr(out_f16), n_elements,
+                                                    _stream(stream)))

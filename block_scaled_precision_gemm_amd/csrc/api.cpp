@@ -45,6 +45,8 @@ struct bsg_plan_s {
   int device;
   char variant[64];
   int tile_m, tile_n, tile_k;
+  void* workspace;          // device memory owned by the plan (split-K partials), or null
+  uint64_t workspace_bytes;
 };
 
 namespace {
@@ -54,6 +56,7 @@ using bsg::set_error;
 // Per-device result of the architecture check, computed once.
 std::mutex g_dev_mutex;
 signed char g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 not
+int g_dev_cus[64];         // compute units of a checked device
 
 bsg_status check_device(int dev) {
   int count = 0;
@@ -75,6 +78,7 @@ bsg_status check_device(int dev) {
       return BSG_ERR_HIP;
     }
     g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_dev_cus[dev] = prop.multiProcessorCount;
     if (g_dev_ok[dev] < 0) {
       set_error("device %d is %s; this library is built for gfx950 (MI355X) only", dev, prop.gcnArchName);
       return BSG_ERR_DEVICE;
@@ -85,6 +89,44 @@ bsg_status check_device(int dev) {
     return BSG_ERR_DEVICE;
   }
   return BSG_OK;
+}
+
+// Split-K factor for a kernel that supports it: enough workgroups to give every compute unit one,
+// while each split keeps at least 4 K tiles.
+int choose_splits(const bsg::KernelVariant& v, int64_t tiles, int64_t K, int cus) {
+  if (v.max_splits <= 1 || tiles >= cus) return 1;
+  const int64_t k_tiles = (K + v.tile_k - 1) / v.tile_k;
+  int64_t s = (cus + tiles - 1) / tiles;
+  if (s > k_tiles / 4) s = k_tiles / 4;
+  if (s > v.max_splits) s = v.max_splits;
+  return s < 1 ? 1 : (int)s;
+}
+
+// hipMalloc / hipFree on `dev`, restoring the caller's current device.
+bsg_status device_alloc(int dev, size_t bytes, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+    set_error("hipSetDevice(%d) failed", dev);
+    return BSG_ERR_HIP;
+  }
+  const hipError_t e = hipMalloc(out, bytes);
+  if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess) {
+    *out = nullptr;
+    set_error("hipMalloc(%zu) of the split-K workspace failed: %s", bytes, hipGetErrorString(e));
+    return BSG_ERR_HIP;
+  }
+  return BSG_OK;
+}
+
+void device_free(int dev, void* p) {
+  if (!p) return;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+  if (cur != dev) (void)hipSetDevice(dev);
+  (void)hipFree(p);
+  if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
 }
 
 bsg_status validate(const bsg_problem* p) {
@@ -209,7 +251,18 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   a.K = (int)problem->K;
   a.tiles_m = (int)((problem->M + v.tile_m - 1) / v.tile_m);
   a.tiles_n = (int)((problem->N + v.tile_n - 1) / v.tile_n);
-  plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n), 1, 1)
+  a.splits = choose_splits(v, (int64_t)a.tiles_m * a.tiles_n, problem->K, g_dev_cus[dev]);
+  if (a.splits > 1) {
+    const size_t bytes = (size_t)a.splits * (size_t)problem->M * (size_t)problem->N * sizeof(float);
+    st = device_alloc(dev, bytes, &plan->workspace);
+    if (st != BSG_OK) {
+      delete plan;
+      return st;
+    }
+    plan->workspace_bytes = bytes;
+    a.ws = (float*)plan->workspace;
+  }
+  plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n * a.splits), 1, 1)
                              : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, 1);
   plan->block = dim3((unsigned)v.block_threads, 1, 1);
   *out_plan = plan;
@@ -269,6 +322,7 @@ bsg_status bsg_plan_destroy(bsg_plan plan) {
     return BSG_ERR_NULL;
   }
   plan->magic = 0;
+  device_free(plan->device, plan->workspace);  // hipFree waits for work still using it
   delete plan;
   return BSG_OK;
 }
@@ -292,7 +346,7 @@ bsg_status bsg_plan_query(bsg_plan plan, bsg_plan_info* info) {
   info->grid_z = plan->grid.z;
   info->block_x = plan->block.x;
   info->lds_bytes = plan->lds_bytes;
-  info->workspace_bytes = 0;
+  info->workspace_bytes = plan->workspace_bytes;
   return BSG_OK;
 }
 

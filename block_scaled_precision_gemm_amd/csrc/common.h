@@ -30,6 +30,8 @@ struct GemmArgs {
   float alpha;
   int M, N, K;
   int tiles_m, tiles_n;   // output tile grid
+  int splits;             // split-K factor (1: none)
+  float* ws;              // split-K partials [splits][M][N] fp32 (plan-owned), or null
 };
 
 // A launcher: enqueues one kernel on `stream` with a precomputed launch shape.  Kernels use static
@@ -42,7 +44,8 @@ struct KernelVariant {
   int tile_m, tile_n, tile_k;
   int block_threads;
   uint32_t lds_bytes;    // static LDS of the kernel (informational)
-  bool linear_grid;      // grid = (tiles_m * tiles_n) workgroups in x; else (tiles_n, tiles_m)
+  bool linear_grid;      // grid = (tiles_m * tiles_n * splits) workgroups in x; else (tiles_n, tiles_m)
+  int max_splits = 1;    // > 1: the kernel supports split-K up to this factor (needs a workspace)
 };
 
 // Variant tables, one per format: index = out dtype (0 bf16, 1 f16) * 4 + bias * 2 + silu.
@@ -52,6 +55,7 @@ const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N);
 const KernelVariant* mxfp8_pipe_variants();
 const KernelVariant* mxfp8_plr_variants();
 const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K);
+const KernelVariant* nvfp4_tiled_variants(int64_t M, int64_t N);
 
 inline int variant_index(Out out, bool bias, bool silu) {
   return (out == Out::F16 ? 4 : 0) + (bias ? 2 : 0) + (silu ? 1 : 0);

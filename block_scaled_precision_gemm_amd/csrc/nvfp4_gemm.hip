@@ -95,6 +95,6 @@ const KernelVariant kDirect[8] = {
 
 }  // namespace
 
-const KernelVariant* nvfp4_variants(int64_t /*M*/, int64_t /*N*/, int64_t /*K*/) { return kDirect; }
+const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t /*K*/) { return nvfp4_tiled_variants(M, N); }
 
 }  // namespace bsg

@@ -30,16 +30,21 @@
  * 625 us per call -- argument building, workspace allocation, can_implement,
  * descriptor initialisation -- is done once, in bsg_plan_create):
  *   bsg_plan_create(problem)  once: validates, picks the kernel variant,
- *                             precomputes grid and kernel arguments.
- *   bsg_run(plan, ...)        per call: O(1) pointer checks and one kernel
- *                             launch on the caller's stream.  No allocation,
- *                             no synchronisation, no device query, so it may
- *                             be captured into a HIP graph.
- *   bsg_plan_destroy(plan)    frees the plan (host memory only).
+ *                             precomputes grid and kernel arguments, and
+ *                             allocates the plan's device workspace if the
+ *                             variant splits K (bsg_plan_info.workspace_bytes).
+ *   bsg_run(plan, ...)        per call: O(1) pointer checks and one or two
+ *                             kernel launches on the caller's stream.  No
+ *                             allocation, no synchronisation, no device query,
+ *                             so it may be captured into a HIP graph.
+ *   bsg_plan_destroy(plan)    frees the plan and its workspace.
  *
  * Ownership: the caller owns every operand buffer, D and the stream; the
- * library owns the plan.  A plan is immutable after creation: concurrent
- * bsg_run calls on one plan from several threads/streams are safe.
+ * library owns the plan and its workspace.  A plan is immutable after
+ * creation.  Concurrent bsg_run calls on one plan are safe when the plan has
+ * no workspace; a plan with a workspace (workspace_bytes > 0) keeps its split-K
+ * partial sums there, so its calls must be ordered (one stream, or events):
+ * overlapping calls on one such plan race.
  *
  * Errors: every function returns a bsg_status and never throws or aborts.
  * On failure nothing is launched and bsg_last_error() (thread-local) holds a
@@ -102,7 +107,7 @@ typedef struct bsg_plan_info {
   int32_t tile_m, tile_n, tile_k;
   uint32_t grid_x, grid_y, grid_z, block_x;
   uint32_t lds_bytes;
-  uint64_t workspace_bytes; /* device workspace the plan owns (0: none) */
+  uint64_t workspace_bytes; /* device workspace the plan owns (0: none); grid_x includes the split-K factor */
 } bsg_plan_info;
 
 /* Validate `problem`, choose the kernel variant for (format, out dtype, epilogue, M bucket) and
@@ -123,8 +128,9 @@ bsg_status bsg_run(bsg_plan plan, const void* A, const void* B, const void* sA, 
 bsg_status bsg_run_alpha_ptr(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB,
                              const float* bias, const float* alpha_dev, void* D, void* stream);
 
-/* Free a plan.  NULL is accepted.  Kernels already enqueued with the plan are unaffected (their
- * arguments were copied at launch). */
+/* Free a plan.  NULL is accepted.  A plan without workspace is host memory only, and kernels already
+ * enqueued with it are unaffected (their arguments were copied at launch).  A plan's workspace is
+ * released with hipFree, which waits for the device's outstanding work first. */
 bsg_status bsg_plan_destroy(bsg_plan plan);
 
 /* Describe the chosen variant.  info->struct_size must be sizeof(bsg_plan_info). */

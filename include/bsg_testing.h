@@ -30,6 +30,14 @@ bsg_status bsg_test_decode_e4m3(const uint8_t* codes, float* out, int64_t n, voi
 bsg_status bsg_test_decode_nvfp4(const uint8_t* packed, const uint8_t* scale_codes, uint16_t* out_bf16,
                                  int64_t n_elements, void* stream);
 
+/* Same layout as bsg_test_decode_nvfp4, through the tiled NVFP4 kernels' fp16 routine:
+ * out_f16[k] = fp16 bits of e2m1(element k) * e4m3(scale_codes[k / 16]) * 2^-7, exact (the factor
+ * 2^-7 keeps every scale inside fp16's range; the GEMM restores it in the epilogue).  A NaN scale
+ * code gives a NaN for its 16 elements.  n_elements: a multiple of 32; packed and out_f16 16-byte
+ * aligned.  Errors: BSG_ERR_SHAPE, BSG_ERR_NULL, BSG_ERR_ALIGN, BSG_ERR_HIP. */
+bsg_status bsg_test_decode_nvfp4_f16(const uint8_t* packed, const uint8_t* scale_codes, uint16_t* out_f16,
+                                     int64_t n_elements, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -199,3 +199,63 @@ def test_plan_info():
     plan = bsg.Plan("mxfp8", 4096, 4096, 4096, out="bf16")
     info = plan.info()
     assert info["workspace_bytes"] == 0 and info["block"] > 0 and info["variant"].startswith("mxfp8")
+
+
+# NVFP4 small-M problems split K across workgroups (fp32 partials in the plan's workspace, summed in
+# split order by a second kernel); these shapes cover split and unsplit plans, ragged M / N and a
+# final half K tile (K % 64 == 32).
+NVFP4_SPLIT_SHAPES = [(100, 80, 1056), (1, 16, 4128), (129, 4000, 2080), (256, 1024, 2048), (640, 4096, 256)]
+
+
+@pytest.mark.parametrize("shape", NVFP4_SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("epi", ["plain", "bias_silu"])
+def test_nvfp4_split_k(shape, epi):
+    M, N, K = shape
+    p = si.problem("nvfp4", M, N, K, seed=900 + M + N + K, bias=epi != "plain", silu=epi != "plain", out="bf16",
+                   alpha=0.75)
+    plan = make_plan(p)
+    info = plan.info()
+    tiles = -(-M // info["tile"][0]) * -(-N // info["tile"][1])
+    splits = info["grid"][0] // tiles
+    assert info["grid"][0] == tiles * splits
+    assert info["workspace_bytes"] == (0 if splits == 1 else splits * M * N * 4)
+    print(f"[plan] {shape} {info['variant']} splits={splits}", flush=True)
+    D = run(p, plan=plan)
+    rep = compare(D, reference(p), p["alpha"], p["silu"], p["out"])
+    assert rep["ok"], rep
+
+
+def test_nvfp4_split_k_deterministic_alpha_ptr_and_graph():
+    p = si.workload("nvfp4_256x4096x4096_loop")
+    plan = make_plan(p)
+    assert plan.info()["workspace_bytes"] > 0
+    dev = to_device(p)
+    D0 = run(p, plan=plan, dev=dev)
+    D1 = run(p, plan=plan, dev=dev)
+    assert np.array_equal(D0, D1)
+    alpha_dev = torch.tensor([float(p["alpha"])], dtype=torch.float32, device="cuda")
+    dev["D"].fill_(0x7FFF)
+    plan.run_alpha_ptr(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha_dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev["D"].cpu().numpy().view(np.uint16), D0)
+    # replayed HIP graphs (both kernels of a call captured) give the eager bits, for each of two sets
+    q = si.workload("nvfp4_256x4096x4096_loop", set_id=1)
+    devq = to_device(q)
+    Dq = run(q, plan=plan, dev=devq)
+    sets = []
+    for d, pp in ((dev, p), (devq, q)):
+        d["D"].fill_(0x7FFF)
+        sets.append(dict(A=d["A"], B=d["B"], sA=d["sA"], sB=d["sB"], D=d["D"], alpha=float(pp["alpha"])))
+    stream = torch.cuda.Stream()
+    bsg.bench_loop(plan, sets, 3, 1, stream)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev["D"].cpu().numpy().view(np.uint16), D0)
+    assert np.array_equal(devq["D"].cpu().numpy().view(np.uint16), Dq)
+
+
+def test_nvfp4_plan_info():
+    plan = bsg.Plan("nvfp4", 128, 8192, 8192, out="bf16", bias=True, silu=True)
+    info = plan.info()
+    assert info["variant"].startswith("nvfp4_tiled")
+    splits = info["grid"][0] // (8192 // info["tile"][1])
+    assert splits > 1 and info["workspace_bytes"] == splits * 128 * 8192 * 4
