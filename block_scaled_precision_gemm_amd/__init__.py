@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_e4m3", "decode_nvfp4", "decode_nvfp4_f16",
+__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_nvfp4_f16",
            "FORMATS", "OUT_DTYPES", "abi_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,8 +62,6 @@ _SIGNATURES = {
     "bsg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bsg_last_error": (ctypes.c_char_p, []),
     "bsg_abi_version": (ctypes.c_int, []),
-    "bsg_test_decode_e4m3": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP]),
-    "bsg_test_decode_nvfp4": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int64, _VP]),
     "bsg_test_decode_nvfp4_f16": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int64, _VP]),
     "bsg_bench_loop": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.POINTER(_VP),
@@ -190,20 +188,8 @@ def bench_loop(plan: Plan, sets: list[dict], calls_per_set: int, mode: int, stre
     return wall.value
 
 
-def decode_e4m3(codes, out, stream=None) -> None:
-    """out[i] (fp32) = device decode of E4M3 code codes[i] (test entry point)."""
-    n = codes.numel() if hasattr(codes, "numel") else len(codes)
-    _check(load_library().bsg_test_decode_e4m3(_ptr(codes), _ptr(out), n, _stream(stream)))
-
-
-def decode_nvfp4(packed, scale_codes, out_bf16, n_elements: int, stream=None) -> None:
-    """out_bf16[k] = device dequantisation of NVFP4 element k (packed[k/2] nibble, scale_codes[k/16])."""
-    _check(load_library().bsg_test_decode_nvfp4(_ptr(packed), _ptr(scale_codes), _ptr(out_bf16), n_elements,
-                                                _stream(stream)))
-
-
 def decode_nvfp4_f16(packed, scale_codes, out_f16, n_elements: int, stream=None) -> None:
-    """out_f16[k] = device fp16 dequantisation of NVFP4 element k times 2^-7, through the tiled
+    """out_f16[k] = device fp16 dequantisation of NVFP4 element k times 2^-8, through the GEMM
     kernels' routine (packed[k/2] nibble, scale_codes[k/16]); n_elements a multiple of 32."""
     _check(load_library().bsg_test_decode_nvfp4_f16(_ptr(packed), _ptr(scale_codes), _ptr(out_f16), n_elements,
                                                     _stream(stream)))

@@ -11,8 +11,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 enum class Fmt : int { MXFP8 = 1, NVFP4 = 2 };
 enum class Out : int { BF16 = 1, F16 = 2 };
@@ -55,7 +53,6 @@ const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N);
 const KernelVariant* mxfp8_pipe_variants();
 const KernelVariant* mxfp8_plr_variants();
 const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K);
-const KernelVariant* nvfp4_tiled_variants(int64_t M, int64_t N);
 
 inline int variant_index(Out out, bool bias, bool silu) {
   return (out == Out::F16 ? 4 : 0) + (bias ? 2 : 0) + (silu ? 1 : 0);

@@ -1,100 +1,373 @@
-// NVFP4 block-scaled GEMM kernels for gfx950.
+// NVFP4 block-scaled GEMM for gfx950.
 //
-// D = epi(alpha * A x B^T (+ bias)), A [M][K/2] and B [N][K/2] packed E2M1 (element 2t in the low
-// nibble of byte t), one E4M3 scale per 16 K elements, global fp32 alpha (the NVFP4 GEMM
-// runNvfp4Gemm<T, kEnableSilu, kEnableBias> of the CUTLASS issue #3003 page).
+// D = epi(alpha * A x B^T (+ bias)): A [M][K/2] and B [N][K/2] packed E2M1 (element 2t in the low
+// nibble of byte t), one E4M3 scale per 16 K elements, a global fp32 alpha (the operation of
+// runNvfp4Gemm<T, kEnableSilu, kEnableBias> on the CUTLASS issue #3003 page).
 //
-// CDNA4's scaled MFMAs take E8M0 (power-of-two) scales per 32 elements; an E4M3 scale per 16 does
-// not fit them exactly.  Instead each element is dequantised in registers to the exact bf16 value
-// e2m1 * e4m3 (at most 6 significant bits, range [2^-10, 2688]) and fed to the bf16 MFMA
-// v_mfma_f32_32x32x16_bf16, so the products the hardware accumulates are exactly the dequantised
-// ones.  The global alpha is applied once, in the epilogue.
+// CDNA4's scaled MFMAs take power-of-two (E8M0) scales per 32 elements, which cannot carry an E4M3
+// scale per 16 elements exactly.  The operands are therefore dequantised on the fly into fp16 and
+// contracted on v_mfma_f32_32x32x16_f16:
+// * element value q * s * 2^-8, exact in fp16 (codec.h): v_cvt_scalef32_pk_f16_fp4 gives q, one
+//   v_pk_mul_f16 applies s * 2^-8; each MFMA product is the exact dequantised product times 2^-16,
+//   accumulated in fp32, and the epilogue multiplies by alpha * 2^16.
 //
-// K order inside the contraction is free as long as A and B use the same order and each element
-// carries its own block's scale.  Each lane therefore loads one contiguous 16-byte chunk (32
-// elements = two scale blocks) per 64-K step and spreads it over four MFMAs:
-//   lane l (r = l % 32, h = l / 32), step c, MFMA t: K elements 64c + 32h + 8t .. +8
-// Register layout of v_mfma_f32_32x32x16_bf16: A lane l holds row r, eight K slots [8h, 8h+8);
-// B likewise for column r; accumulator element i: column r, row 8*(i/4) + 4*h + (i%4).
+// Work split.  A workgroup tile has a "shared" side of 128 rows and a "private" side of 256 rows:
+// with SHARED_A the tile is 128 (M) x 256 (N), otherwise 256 (M) x 128 (N).  Eight waves (two per
+// SIMD: one wave alone issues VALU work at about half rate and cannot overlap it with its own MFMAs)
+// each compute 64 shared x 64 private outputs (2 x 2 accumulators of 32 x 32).
+// * The shared operand is decoded once per K tile by all 512 threads (8 bytes = 16 elements = one
+//   scale block each) into a double-buffered fp16 LDS tile, read by the waves as MFMA fragments.
+// * Each wave decodes its private rows straight into MFMA registers: with the K order inside a
+//   64-element tile permuted so that lane l (r = l % 32, h = l / 32) covers elements 32h .. 32h+31,
+//   one 16-byte chunk per lane per 32-row block holds exactly the four fragments of that block.  The
+//   shared fragments use the same permutation.  (Each private row is decoded by the two waves that
+//   share it.)
+// * Packed bytes and scale codes of K tile k+DIST are copied global -> LDS by buffer_load ... lds
+//   (ring of DIST+1 stages) while tile k is computed and tile k+1's shared rows are decoded; one
+//   barrier per K tile, after each wave has waited for its own copies of tile k+2.  Rows past M / N
+//   read as zeros through the buffer range check; the missing half of a final half tile
+//   (K % 64 == 32) decodes with scale code 0, i.e. as zeros.
+// * Split-K for small M x N: the grid holds tiles x S workgroups; split s covers K tiles
+//   [s KT / S, (s+1) KT / S) and writes its raw fp32 accumulators to a plan-owned workspace
+//   [S][M][N]; a second kernel sums the S partials in split order (deterministic), applies the
+//   epilogue and writes D.  With S == 1 the epilogue runs in the GEMM kernel.
+//
+// v_mfma_f32_32x32x16_f16 register layout: A lane l (r = l % 32, h = l / 32) holds row r, K
+// slots [8h, 8h+8) of the 16-slot slice; B likewise for column r; accumulator element e of lane l:
+// row 8*(e/4) + 4h + e%4, column r.  Here slice s of a tile maps slot 8h + t to tile element
+// 32h + 8s + t, the same for A and B, so the contraction covers each element once.
+//
+// LDS layouts (bank-conflict free for the access patterns named):
+// * raw stage: row R's 32 packed bytes at 32R, its half h at +16 (h ^ ((R >> 3) & 1)) (fragment
+//   reads: 16 lanes = 16 rows x one half); the two scale codes of row R, half h at 8R + 4h (a
+//   2-byte buffer_load ... lds fills a 4-byte LDS slot per lane, zero-extended).
+// * decoded shared stage: row R = 128 bytes = 8 pieces of 8 fp16 (piece p = elements 8p .. 8p+7),
+//   piece p stored at p ^ ((R >> 1) & 7) (decode stores: 8 rows x 2 halves per 16 lanes; fragment
+//   reads: 16 rows x one piece).
 #include "codec.h"
 #include "common.h"
 #include "epilogue.h"
 
 namespace bsg {
-namespace {
+namespace nvr {
 
-__device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+constexpr int BK = 64;                       // K elements per tile
+constexpr int BS = 128, BP = 256;            // shared / private rows per workgroup tile
+constexpr int THREADS = 512, WAVES = 8;  // two waves per SIMD
+constexpr int DIST = 3, NR = DIST + 1;       // copies run DIST tiles ahead; raw ring stages
+constexpr int ROWS = BS + BP;                // rows copied per K tile
+constexpr int RAW_DATA = ROWS * 32;          // 12 KiB
+constexpr int RAW_STAGE = RAW_DATA + ROWS * 8;  // + scale codes, 8 bytes per row
+constexpr int DEC_STAGE = BS * 128;          // 16 KiB
+constexpr int LDS_BYTES = NR * RAW_STAGE + 2 * DEC_STAGE;
+constexpr int COPIES = 4;                    // buffer_load ... lds per wave per K tile
+constexpr int TS = 2, TP = 2;                // 2 shared x 2 private MFMA blocks (64 x 64) per wave
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any operand's size (< 2^31)
+constexpr float kRescale = 65536.0f;           // 2^16: undoes the 2^-8 of both fp16 operands
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ v16f mfma_f16(v4i a, v4i b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------------------------------------
-// Direct kernel: 4 waves, 64x64 tile per workgroup, 32x32 per wave, operands decoded straight
-// from global memory.  Any M >= 1, N % 16 == 0, K % 32 == 0.
-// ---------------------------------------------------------------------------------------------
-template <Out O, bool BIAS, bool SILU>
-__global__ __launch_bounds__(256) void nvfp4_direct_kernel(GemmArgs p) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 31, h = lane >> 5;
-  const int m0 = blockIdx.y * 64 + (wave >> 1) * 32;
-  const int n0 = blockIdx.x * 64 + (wave & 1) * 32;
-  const int K = p.K, KH = K >> 1, KB = K >> 4;
-  const int arow = min(m0 + r, p.M - 1);
-  const int brow = min(n0 + r, p.N - 1);
-  const uint8_t* ap = p.A + (size_t)arow * KH + 16 * h;
-  const uint8_t* bp = p.B + (size_t)brow * KH + 16 * h;
-  const uint8_t* sap = p.sA + (size_t)arow * KB + 2 * h;
-  const uint8_t* sbp = p.sB + (size_t)brow * KB + 2 * h;
-  v16f acc = {};
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    v4i qa = {0, 0, 0, 0}, qb = {0, 0, 0, 0};
-    float sa0 = 0.f, sa1 = 0.f, sb0 = 0.f, sb1 = 0.f;
-    if (k0 + 32 * h < K) {  // K % 32 == 0: a lane's 32-element chunk is all in or all out
-      qa = *(const v4i*)(ap + (k0 >> 1));
-      qb = *(const v4i*)(bp + (k0 >> 1));
-      const int kb = k0 >> 4;
-      sa0 = e4m3_to_f32(sap[kb]);
-      sa1 = e4m3_to_f32(sap[kb + 1]);
-      sb0 = e4m3_to_f32(sbp[kb]);
-      sb1 = e4m3_to_f32(sbp[kb + 1]);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const v4i a = e2m1x8_scaled_bf16x8((uint32_t)qa[t], t < 2 ? sa0 : sa1);
-      const v4i b = e2m1x8_scaled_bf16x8((uint32_t)qb[t], t < 2 ? sb0 : sb1);
-      acc = mfma_bf16_32x32x16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), acc);
-    }
+// Wait until at most N of this wave's buffer loads (here: global -> LDS copies) are in flight.  The
+// compiler does not see the LDS writes of those copies; the memory clobber keeps every LDS access
+// on its side of the wait.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait for this wave's LDS accesses, then meet the other waves (outstanding copies stay in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// XCD-aware order for the unsplit grid: consecutive workgroup ids go to different XCDs, so give each
+// XCD a contiguous range of tile ids, walked in groups of 8 tile-rows.
+__device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
+  const int T = tiles_m * tiles_n;
+  int id = bid;
+  if ((T & 7) == 0) id = (bid & 7) * (T >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = id / per_group;
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = id - group * per_group;
+  return make_int2(first_m + in_group % gsize, in_group / gsize);
+}
+
+template <bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT>
+__global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
+  constexpr int BM = SHARED_A ? BS : BP, BN = SHARED_A ? BP : BS;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  uint8_t* const raw = lds;
+  uint8_t* const dec = lds + NR * RAW_STAGE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn, split = 0;
+  if constexpr (SPLIT) {
+    split = (int)blockIdx.x % p.splits;
+    const int t = (int)blockIdx.x / p.splits;
+    tm = t / p.tiles_n;
+    tn = t - tm * p.tiles_n;
+  } else {
+    const int2 t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n);
+    tm = t.x;
+    tn = t.y;
   }
-  const int n = n0 + r;
-  if (n >= p.N) return;
-  const float alpha = load_alpha(p);
-  const float bv = BIAS ? p.bias[n] : 0.0f;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int K = p.K, KT = (K + BK - 1) / BK;
+  const int kb = SPLIT ? (int)((int64_t)split * KT / p.splits) : 0;
+  const int ke = SPLIT ? (int)((int64_t)(split + 1) * KT / p.splits) : KT;
+  const uint32_t KH = (uint32_t)K >> 1, KS = (uint32_t)K >> 4;
+
+  // Buffer resources of the shared and private operand rows of this tile (rows past M / N fall
+  // outside the range and read as zeros).
+  const uint8_t* s_q = SHARED_A ? p.A + (size_t)m0 * KH : p.B + (size_t)n0 * KH;
+  const uint8_t* s_s = SHARED_A ? p.sA + (size_t)m0 * KS : p.sB + (size_t)n0 * KS;
+  const uint8_t* p_q = SHARED_A ? p.B + (size_t)n0 * KH : p.A + (size_t)m0 * KH;
+  const uint8_t* p_s = SHARED_A ? p.sB + (size_t)n0 * KS : p.sA + (size_t)m0 * KS;
+  const int s_rows = SHARED_A ? min(BS, p.M - m0) : min(BS, p.N - n0);
+  const int p_rows = SHARED_A ? min(BP, p.N - n0) : min(BP, p.M - m0);
+  const __amdgpu_buffer_rsrc_t rs_q =
+      __builtin_amdgcn_make_buffer_rsrc((void*)s_q, (short)0, (int)(s_rows * KH), (int)kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_s =
+      __builtin_amdgcn_make_buffer_rsrc((void*)s_s, (short)0, (int)(s_rows * KS), (int)kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rp_q =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p_q, (short)0, (int)(p_rows * KH), (int)kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rp_s =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p_s, (short)0, (int)(p_rows * KS), (int)kRsrcWord3);
+
+  // Wave roles: shared half wsh (shared rows 64 wsh .. +64), private quarter wp (private rows
+  // 64 wp .. +64); the wave computes those 64 x 64 outputs.
+  const int wsh = wave & 1, wp = wave >> 1;
+
+  // Copy plan.  A K tile needs 24 copies: data copies of 32 rows x 32 bytes (lane l: row 32q + l/2,
+  // half (l & 1) ^ ((R >> 3) & 1), 16 bytes at 1 KiB * q + 16 l; q = 0..3 shared, 4..11 private) and
+  // their scale copies (lane l: the 2 codes of that row's half l & 1 into the 4-byte slot at
+  // 256 q + 4 l = 8R + 4 (l & 1)).  Wave w issues copies q2 = w + (w & 4) (shared copies 0..3 for
+  // w < 4; for w >= 4 a repeat of its own private copies, which writes the same bytes to the same
+  // place) and its private copies q = 4 + w: the same four copies in every wave, without branches or
+  // selected LDS addresses (either would make the compiler drain all copies before LDS reads).
+  const int qp = 4 + wave, qs = wave + (wave & 4);
+  const bool has_shared = wave < 4;
+  auto copy_off = [&](int q, bool data, uint32_t& off, int& half) {
+    const int R = 32 * q + (lane >> 1);
+    const int row = q < 4 ? R : R - BS;  // row within its operand's tile rows
+    half = data ? (lane & 1) ^ ((R >> 3) & 1) : (lane & 1);
+    off = data ? (uint32_t)row * KH + 16u * half : (uint32_t)row * KS + 2u * half;
+  };
+  uint32_t o_pd, o_ps, o_sd, o_ss;
+  int h_unused;
+  copy_off(qp, true, o_pd, h_unused);
+  copy_off(qp, false, o_ps, h_unused);
+  copy_off(qs, true, o_sd, h_unused);
+  copy_off(qs, false, o_ss, h_unused);
+  const __amdgpu_buffer_rsrc_t r2_q = has_shared ? rs_q : rp_q;
+  const __amdgpu_buffer_rsrc_t r2_s = has_shared ? rs_s : rp_s;
+  // Copy offsets are loop-invariant (so the compiler's wait bookkeeping stays exact).  The missing
+  // half of a final half tile (K % 64 == 32) is still copied -- the next row's first bytes, or zeros
+  // past the range for the last row -- and the decode gives it scale code 0, i.e. zero elements.
+  auto copy_tile = [&](int kt) {
+    kt = min(kt, ke - 1);  // past the last tile re-read it (never consumed): uniform load counts
+    uint8_t* st = raw + (kt % NR) * RAW_STAGE;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_q, (lds_void*)(st + 1024 * qs), 16, o_sd, (uint32_t)kt * 32u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_s, (lds_void*)(st + RAW_DATA + 256 * qs), 2, o_ss, (uint32_t)kt * 4u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_q, (lds_void*)(st + 1024 * qp), 16, o_pd, (uint32_t)kt * 32u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_s, (lds_void*)(st + RAW_DATA + 256 * qp), 2, o_ps, (uint32_t)kt * 4u, 0, 0);
+  };
+  // Scale codes of half h of K tile kt, or 0 when that half lies past K.
+  auto half_scales = [&](uint32_t codes, int kt, int h) -> uint32_t { return kt * BK + 32 * h < K ? codes : 0u; };
+
+  // Shared decode: thread t takes shared row t/4, quarter t&3 (half (t&3)/2, 8 bytes = one scale
+  // block), and writes its two decoded pieces 4h + 2 sub + {0, 1}.
+  const int sd_row = tid >> 2, sd_h = (tid >> 1) & 1, sd_sub = tid & 1;
+  const uint32_t sd_raw = (uint32_t)(32 * sd_row + 16 * (sd_h ^ ((sd_row >> 3) & 1)));
+  const uint32_t sd_scale = (uint32_t)(RAW_DATA + 8 * sd_row + 4 * sd_h);
+  uint32_t sd_out[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+    sd_out[d] = (uint32_t)(128 * sd_row + (((4 * sd_h + 2 * sd_sub + d) ^ ((sd_row >> 1) & 7)) << 4));
+  auto decode_shared = [&](int kt) {
+    const uint8_t* st = raw + (kt % NR) * RAW_STAGE;
+    uint8_t* out = dec + (kt & 1) * DEC_STAGE;
+    const v4i q4 = *(const v4i*)(st + sd_raw);  // the whole half; this thread uses 8 of its 16 bytes
+    const uint2 q = sd_sub ? make_uint2((uint32_t)q4[2], (uint32_t)q4[3]) : make_uint2((uint32_t)q4[0], (uint32_t)q4[1]);
+    const uint32_t s = e4m3x2_scale_f16x2(half_scales(*(const uint32_t*)(st + sd_scale), kt, sd_h));
+    const uint32_t s2 = sd_sub ? f16x2_splat_hi(s) : f16x2_splat_lo(s);
+    *(v4i*)(out + sd_out[0]) = e2m1x8_scaled_f16x8(q.x, s2);
+    *(v4i*)(out + sd_out[1]) = e2m1x8_scaled_f16x8(q.y, s2);
+  };
+
+  // Fragment addressing.  Private block j: stage row 128 + 64 wp + 32j + r, the lane's half hl.
+  const int r32 = lane & 31, hl = lane >> 5;
+  uint32_t pf_raw[TP], pf_scale[TP];
+#pragma unroll
+  for (int j = 0; j < TP; ++j) {
+    const int R = BS + 64 * wp + 32 * j + r32;
+    pf_raw[j] = (uint32_t)(32 * R + 16 * (hl ^ ((R >> 3) & 1)));
+    pf_scale[j] = (uint32_t)(RAW_DATA + 8 * R + 4 * hl);
+  }
+  // Shared block i, slice s: decoded row 64 wsh + 32i + r, piece 4 hl + s.
+  const uint32_t sf_row = (uint32_t)(128 * (64 * wsh + r32));
+  const int sf_sw = (r32 >> 1) & 7;  // (64 wsh + 32i + r) >> 1 & 7 does not depend on wsh, i
+  uint32_t sf_piece[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) sf_piece[s] = (uint32_t)(((4 * hl + s) ^ sf_sw) << 4);
+
+  v16f acc[TS][TP];
+#pragma unroll
+  for (int i = 0; i < TS; ++i)
+#pragma unroll
+    for (int j = 0; j < TP; ++j) acc[i][j] = v16f{};
+
+  // One K tile: tile kt+1's shared rows are decoded into the other decoded buffer; tile kt's private
+  // rows are decoded into registers slice by slice, one slice ahead of the MFMAs that use them.
+  auto step = [&](int kt) {
+    decode_shared(kt + 1);  // past the last tile: stale bytes into a buffer nobody reads
+    const uint8_t* st = raw + (kt % NR) * RAW_STAGE;
+    const uint8_t* dst = dec + (kt & 1) * DEC_STAGE;
+    v4i pq[TP];
+    uint32_t ps[TP][2];
+#pragma unroll
+    for (int j = 0; j < TP; ++j) {
+      pq[j] = *(const v4i*)(st + pf_raw[j]);
+      const uint32_t s = e4m3x2_scale_f16x2(half_scales(*(const uint32_t*)(st + pf_scale[j]), kt, hl));
+      ps[j][0] = f16x2_splat_lo(s);
+      ps[j][1] = f16x2_splat_hi(s);
+    }
+    v4i pf[2][TP], sf[2][TS];
+#pragma unroll
+    for (int j = 0; j < TP; ++j) pf[0][j] = e2m1x8_scaled_f16x8((uint32_t)pq[j][0], ps[j][0]);
+#pragma unroll
+    for (int i = 0; i < TS; ++i) sf[0][i] = *(const v4i*)(dst + sf_row + 32 * 128 * i + sf_piece[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = s & 1, n = c ^ 1;
+      if (s < 3) {
+#pragma unroll
+        for (int i = 0; i < TS; ++i) sf[n][i] = *(const v4i*)(dst + sf_row + 32 * 128 * i + sf_piece[s + 1]);
+#pragma unroll
+        for (int j = 0; j < TP; ++j) pf[n][j] = e2m1x8_scaled_f16x8((uint32_t)pq[j][s + 1], ps[j][(s + 1) >> 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < TS; ++i)
+#pragma unroll
+        for (int j = 0; j < TP; ++j)
+          acc[i][j] = SHARED_A ? mfma_f16(sf[c][i], pf[c][j], acc[i][j]) : mfma_f16(pf[c][j], sf[c][i], acc[i][j]);
+    }
+  };
+
+  // Prologue: copies of tiles kb .. kb+DIST-1 (clamped); tile kb's shared rows decoded.
+#pragma unroll
+  for (int i = 0; i < DIST; ++i) copy_tile(kb + i);
+  wait_copies<(DIST - 1) * COPIES>();
+  lds_barrier();  // every wave's copies of tile kb have landed
+  decode_shared(kb);
+  wait_copies<(DIST - 2) * COPIES>();
+  lds_barrier();  // tile kb decoded, tile kb+1 landed
+  // Steady state: step kt issues tile kt+DIST's copies, computes tile kt and decodes tile kt+1's
+  // shared rows; before the barrier that ends it, the wave's copies of tile kt+2 must have landed
+  // (tiles kt+3 .. kt+DIST may stay in flight).  Raw stages in use: kt .. kt+DIST: NR = DIST + 1.
+  int kt = kb;
+#pragma unroll 1
+  for (; kt + DIST < ke; ++kt) {
+    copy_tile(kt + DIST);
+    step(kt);
+    wait_copies<(DIST - 2) * COPIES>();
+    lds_barrier();
+  }
+  // Last DIST tiles: nothing left to copy.  Leaves no copy in flight past the end of the kernel.
+#pragma unroll 1
+  for (; kt < ke; ++kt) {
+    step(kt);
+    wait_copies<0>();
+    lds_barrier();
+  }
+
+  // Epilogue.  SHARED_A: acc[i][j] covers m = m0 + 64 wsh + 32i + 8*(e/4) + 4*hl + e%4 and
+  // n = n0 + 64 wp + 32j + r32; otherwise m = m0 + 64 wp + 32j + 8*(e/4) + 4*hl + e%4 and
+  // n = n0 + 64 wsh + 32i + r32.
+  const float alpha = load_alpha(p) * kRescale;
   uint16_t* D = (uint16_t*)p.D;
+  float* ws = SPLIT ? p.ws + (size_t)split * p.M * p.N : nullptr;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m = m0 + 8 * (i >> 2) + 4 * h + (i & 3);
-    if (m < p.M) D[(size_t)m * p.N + n] = to_out_bits<O>(epi_value<SILU>(acc[i], alpha, bv));
-  }
+  for (int i = 0; i < TS; ++i)
+#pragma unroll
+    for (int j = 0; j < TP; ++j) {
+      const int mb = SHARED_A ? m0 + 64 * wsh + 32 * i : m0 + 64 * wp + 32 * j;
+      const int n = SHARED_A ? n0 + 64 * wp + 32 * j + r32 : n0 + 64 * wsh + 32 * i + r32;
+      if (n >= p.N) continue;
+      const float bv = (!SPLIT && BIAS) ? p.bias[n] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = mb + 8 * (e >> 2) + 4 * hl + (e & 3);
+        if (m >= p.M) continue;
+        if constexpr (SPLIT)
+          ws[(size_t)m * p.N + n] = acc[i][j][e];
+        else
+          D[(size_t)m * p.N + n] = to_out_bits<O>(epi_value<SILU>(acc[i][j][e], alpha, bv));
+      }
+    }
 }
 
+// Split-K finish: D[m][n] = epi(alpha * 2^16 * sum_s ws[s][m][n] (+ bias[n])), summed in split
+// order.  One thread per 4 consecutive columns (N % 16 == 0).
 template <Out O, bool BIAS, bool SILU>
-hipError_t launch_direct(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
-  void* kargs[] = {(void*)&args};
-  return hipLaunchKernel((const void*)&nvfp4_direct_kernel<O, BIAS, SILU>, grid, block, kargs, 0, stream);
+__global__ __launch_bounds__(256) void nvfp4_splitk_finish_kernel(GemmArgs p) {
+  const int nq = p.N >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.M * nq) return;
+  const int m = (int)(idx / nq), n = (int)(idx - (int64_t)m * nq) * 4;
+  const size_t plane = (size_t)p.M * p.N;
+  const float* src = p.ws + (size_t)m * p.N + n;
+  v4f s = *(const v4f*)src;
+  for (int k = 1; k < p.splits; ++k) s += *(const v4f*)(src + k * plane);
+  const float alpha = load_alpha(p) * kRescale;
+  v4f b = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};  // bias: 4-byte aligned
+  uint32_t* D = (uint32_t*)((uint16_t*)p.D + (size_t)m * p.N + n);
+  D[0] = pack2_out<O>(epi_value<SILU>(s[0], alpha, b[0]), epi_value<SILU>(s[1], alpha, b[1]));
+  D[1] = pack2_out<O>(epi_value<SILU>(s[2], alpha, b[2]), epi_value<SILU>(s[3], alpha, b[3]));
 }
 
-#define BSG_NV_DIRECT(O, B, S) \
-  { "nvfp4_direct_64x64", &launch_direct<O, B, S>, 64, 64, 64, 256, 0, false }
-const KernelVariant kDirect[8] = {
-    BSG_NV_DIRECT(Out::BF16, false, false), BSG_NV_DIRECT(Out::BF16, false, true),
-    BSG_NV_DIRECT(Out::BF16, true, false),  BSG_NV_DIRECT(Out::BF16, true, true),
-    BSG_NV_DIRECT(Out::F16, false, false),  BSG_NV_DIRECT(Out::F16, false, true),
-    BSG_NV_DIRECT(Out::F16, true, false),   BSG_NV_DIRECT(Out::F16, true, true),
-};
-#undef BSG_NV_DIRECT
+template <bool SHARED_A, Out O, bool BIAS, bool SILU>
+hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
+  void* kargs[] = {(void*)&args};
+  if (args.splits <= 1)
+    return hipLaunchKernel((const void*)&nvfp4_kernel<SHARED_A, O, BIAS, SILU, false>, grid, block, kargs, 0, stream);
+  hipError_t e =
+      hipLaunchKernel((const void*)&nvfp4_kernel<SHARED_A, O, BIAS, SILU, true>, grid, block, kargs, 0, stream);
+  if (e != hipSuccess) return e;
+  const int64_t threads = (int64_t)args.M * (args.N >> 2);
+  return hipLaunchKernel((const void*)&nvfp4_splitk_finish_kernel<O, BIAS, SILU>,
+                         dim3((unsigned)((threads + 255) / 256)), dim3(256), kargs, 0, stream);
+}
 
-}  // namespace
+#define BSG_NVR(SA, NAME, O, B, S) \
+  { NAME, &launch<SA, O, B, S>, SA ? BS : BP, SA ? BP : BS, BK, THREADS, (uint32_t)LDS_BYTES, true, 16 }
+#define BSG_NVR_TABLE(SA, NAME)                                                              \
+  {                                                                                           \
+    BSG_NVR(SA, NAME, Out::BF16, false, false), BSG_NVR(SA, NAME, Out::BF16, false, true),    \
+        BSG_NVR(SA, NAME, Out::BF16, true, false), BSG_NVR(SA, NAME, Out::BF16, true, true),  \
+        BSG_NVR(SA, NAME, Out::F16, false, false), BSG_NVR(SA, NAME, Out::F16, false, true),  \
+        BSG_NVR(SA, NAME, Out::F16, true, false), BSG_NVR(SA, NAME, Out::F16, true, true),    \
+  }
+const KernelVariant kSharedA[8] = BSG_NVR_TABLE(true, "nvfp4_128x256_sharedA");
+const KernelVariant kSharedB[8] = BSG_NVR_TABLE(false, "nvfp4_256x128_sharedB");
+#undef BSG_NVR_TABLE
+#undef BSG_NVR
 
-const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t /*K*/) { return nvfp4_tiled_variants(M, N); }
+}  // namespace nvr
+
+// One 128-row tile of A (small M): A is the shared side; otherwise B is.
+const KernelVariant* nvfp4_variants(int64_t M, int64_t /*N*/, int64_t /*K*/) {
+  return M <= nvr::BS ? nvr::kSharedA : nvr::kSharedB;
+}
 
 }  // namespace bsg

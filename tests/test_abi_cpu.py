@@ -76,11 +76,10 @@ def test_null_arguments():
     assert lib.bsg_run(None, 1, 1, 1, 1, None, 1.0, 1, None) == 1
     assert lib.bsg_plan_destroy(None) == 0
     assert lib.bsg_plan_query(None, None) == 1
-    assert lib.bsg_test_decode_e4m3(None, None, 0, None) == 0
-    assert lib.bsg_test_decode_e4m3(None, None, 4, None) == 1
-    assert lib.bsg_test_decode_nvfp4(None, None, None, -16, None) == 2
-    assert lib.bsg_test_decode_nvfp4(None, None, None, 24, None) == 2
-    assert lib.bsg_test_decode_nvfp4(None, None, None, 32, None) == 1
+    assert lib.bsg_test_decode_nvfp4_f16(None, None, None, 0, None) == 0
+    assert lib.bsg_test_decode_nvfp4_f16(None, None, None, -32, None) == 2
+    assert lib.bsg_test_decode_nvfp4_f16(None, None, None, 48, None) == 2
+    assert lib.bsg_test_decode_nvfp4_f16(None, None, None, 32, None) == 1
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -256,6 +256,6 @@ def test_nvfp4_split_k_deterministic_alpha_ptr_and_graph():
 def test_nvfp4_plan_info():
     plan = bsg.Plan("nvfp4", 128, 8192, 8192, out="bf16", bias=True, silu=True)
     info = plan.info()
-    assert info["variant"].startswith("nvfp4_tiled")
+    assert info["variant"].startswith("nvfp4_")
     splits = info["grid"][0] // (8192 // info["tile"][1])
     assert splits > 1 and info["workspace_bytes"] == splits * 128 * 8192 * 4
