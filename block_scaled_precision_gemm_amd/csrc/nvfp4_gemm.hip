@@ -66,6 +66,7 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any operand's size (< 2^31)
 constexpr float kRescale = 65536.0f;           // 2^16: undoes the 2^-8 of both fp16 operands
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+static_assert(WAVES * 32 * 72 * 4 <= LDS_BYTES, "epilogue staging");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -290,30 +291,51 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     lds_barrier();
   }
 
-  // Epilogue.  SHARED_A: acc[i][j] covers m = m0 + 64 wsh + 32i + 8*(e/4) + 4*hl + e%4 and
-  // n = n0 + 64 wp + 32j + r32; otherwise m = m0 + 64 wp + 32j + 8*(e/4) + 4*hl + e%4 and
-  // n = n0 + 64 wsh + 32i + r32.
+  // Epilogue, staged through LDS (free now: the last barrier has passed and no copy is in flight).
+  // The wave's 64 x 64 block -- SHARED_A: rows m0 + 64 wsh + .., columns n0 + 64 wp + ..; otherwise
+  // rows m0 + 64 wp + .., columns n0 + 64 wsh + .. -- goes out in two passes of 32 rows: accumulator
+  // element e of block (i, j) is row 32 mi + 8*(e/4) + 4*hl + e%4, column 32 ni + r32 (mi, ni = i, j
+  // for SHARED_A, else j, i).  Rows are EPI_STRIDE floats apart (4 * 72 = 32 mod 64 banks: the two
+  // rows a store instruction touches land on different banks); each lane then reads 4 consecutive
+  // columns and the wave stores 4 full rows per instruction.
+  constexpr int EPI_STRIDE = 72;
+  float* stage = (float*)lds + wave * (32 * EPI_STRIDE);
+  const int mw = m0 + 64 * (SHARED_A ? wsh : wp), nw = n0 + 64 * (SHARED_A ? wp : wsh);
   const float alpha = load_alpha(p) * kRescale;
-  uint16_t* D = (uint16_t*)p.D;
-  float* ws = SPLIT ? p.ws + (size_t)split * p.M * p.N : nullptr;
 #pragma unroll
-  for (int i = 0; i < TS; ++i)
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int j = 0; j < TP; ++j) {
-      const int mb = SHARED_A ? m0 + 64 * wsh + 32 * i : m0 + 64 * wp + 32 * j;
-      const int n = SHARED_A ? n0 + 64 * wp + 32 * j + r32 : n0 + 64 * wsh + 32 * i + r32;
-      if (n >= p.N) continue;
-      const float bv = (!SPLIT && BIAS) ? p.bias[n] : 0.0f;
+    for (int i = 0; i < TS; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = mb + 8 * (e >> 2) + 4 * hl + (e & 3);
-        if (m >= p.M) continue;
-        if constexpr (SPLIT)
-          ws[(size_t)m * p.N + n] = acc[i][j][e];
-        else
-          D[(size_t)m * p.N + n] = to_out_bits<O>(epi_value<SILU>(acc[i][j][e], alpha, bv));
+      for (int j = 0; j < TP; ++j) {
+        const int mi = SHARED_A ? i : j, ni = SHARED_A ? j : i;
+        if (mi != pass) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          stage[(8 * (e >> 2) + 4 * hl + (e & 3)) * EPI_STRIDE + 32 * ni + r32] = acc[i][j][e];
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c4 = 4 * (lane & 15);
+    const int n = nw + c4;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = 4 * it + (lane >> 4);
+      const int m = mw + 32 * pass + row;
+      const v4f v = *(const v4f*)(stage + row * EPI_STRIDE + c4);
+      if (m >= p.M || n >= p.N) continue;  // N % 16 == 0: a lane's 4 columns are all in or all out
+      if constexpr (SPLIT) {
+        *(v4f*)(p.ws + (size_t)split * p.M * p.N + (size_t)m * p.N + n) = v;
+      } else {
+        v4f b = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
+        uint2 o;
+        o.x = pack2_out<O>(epi_value<SILU>(v[0], alpha, b[0]), epi_value<SILU>(v[1], alpha, b[1]));
+        o.y = pack2_out<O>(epi_value<SILU>(v[2], alpha, b[2]), epi_value<SILU>(v[3], alpha, b[3]));
+        *(uint2*)((uint16_t*)p.D + (size_t)m * p.N + n) = o;
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass overwrites
+  }
 }
 
 // Split-K finish: D[m][n] = epi(alpha * 2^16 * sum_s ws[s][m][n] (+ bias[n])), summed in split
