@@ -14,6 +14,7 @@ The CPU baseline is the fp64 oracle (test infrastructure) timed on the host core
 of rows of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-main] [--calibration-copy]
+       python bench.py --counters-from FETCH_CSV WRITE_CSV   (records HBM traffic from rocprofv3 passes)
 """
 from __future__ import annotations
 
@@ -33,13 +34,59 @@ HBM_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "mxfp8_4096_counters.json")
 
 
+# Sources of the headline kernel (mxfp8_plr): committed counters are valid only for these bytes.
+HEADLINE_SOURCES = ("mxfp8_plr.hip", "common.h", "epilogue.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "block_scaled_precision_gemm_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    for name in HEADLINE_SOURCES:
+        with open(os.path.join(ROOT, "block_scaled_precision_gemm_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def write_counters(fetch_csv: str, write_csv: str) -> int:
+    """Turn two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; each over `bench.py --only-main
+    --calibration-copy`) into profiles/mxfp8_4096_counters.json.  FETCH_SIZE / WRITE_SIZE are scaled by
+    what they read for the 256 MiB device copy of known size."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in vals.items()}
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    gemm = [k for k in fetch if "mxfp8_plr_kernel" in k]
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if len(gemm) != 1 or len(copy) != 1:
+        print(f"expected one GEMM and one copy kernel, got {list(fetch)}", file=sys.stderr)
+        return 1
+    g, c = gemm[0], copy[0]
+    n = float(1 << 28)
+    rf, wf = n / (fetch[c] * 1024), n / (write[c] * 1024)
+    traffic = fetch[g] * 1024 * rf + write[g] * 1024 * wf
+    M = N = K = 4096
+    out = {
+        "kernel": g, "workload": "MXFP8 4096^3 bf16 alpha 0.5",
+        "fetch_kib_per_dispatch": fetch[g], "write_kib_per_dispatch": write[g],
+        "copy_calibration": {"bytes_read": n, "bytes_written": n, "fetch_kib": fetch[c], "write_kib": write[c],
+                             "read_factor": rf, "write_factor": wf},
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_bytes_per_launch": M * K + N * K + (M + N) * K // 32 + 2 * M * N,
+        "source_hash": kernel_source_hash(),
+        "commands": [f"rocprofv3 --pmc {x} -f csv -d <repo>/gpurun_out/pmc_{x.lower()} -o run -- python3 <repo>/bench.py "
+                     "--only-main --steps 20 --warmup 5 --calibration-copy" for x in ("FETCH_SIZE", "WRITE_SIZE")],
+    }
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
 
 
 def log(msg: str) -> None:
@@ -161,7 +208,11 @@ def main() -> int:
     ap.add_argument("--only-main", action="store_true", help="time the headline workload only (for profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run a device copy of known size (HBM counter calibration)")
+    ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: write the headline kernel's HBM-traffic record from two rocprofv3 passes")
     args = ap.parse_args()
+    if args.counters_from:
+        return write_counters(*args.counters_from)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)

@@ -210,12 +210,18 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_plr_kernel(GemmArgs p) {
     for (int i = 0; i < TM; ++i) ssa[i] = (int)(sa[i][u >> 1] >> shift);
 #pragma unroll
     for (int j = 0; j < TN; ++j) ssb[j] = (int)(sb[j][u >> 1] >> shift);
-    // tile kt+1 is in stage (u+1)%4 for every wave; every wave has finished reading stage u%4
+    // tile kt+1 is in stage (u+1)%4 for every wave; every wave has finished reading stage u%4.
+    // MFMAs touch no memory, so without a scheduling barrier the previous tile's would sink below
+    // this wait and push this tile's fragment reads towards the next one.
+    __builtin_amdgcn_sched_barrier(0);
     wait_barrier<loads_after(u)>();
     copy_tile(kt + 4, u % NS);
     if constexpr (u == 1) copy_scales(kb / UNROLL + 1);
     read_frags((u + 1) % NS, nxt);
     if constexpr (u == UNROLL - 1) read_scales();  // next batch, for tile kt+1
+    // keep those reads ahead of this tile's MFMAs: issued late, they would still be in flight at the
+    // next barrier, whose lgkmcnt(0) would then stall on them
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
