@@ -63,7 +63,6 @@ constexpr int LDS_BYTES = NR * RAW_STAGE + 2 * DEC_STAGE;
 constexpr int COPIES = 4;                    // buffer_load ... lds per wave per K tile
 constexpr int TS = 2, TP = 2;                // 2 shared x 2 private MFMA blocks (64 x 64) per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any operand's size (< 2^31)
 constexpr float kRescale = 65536.0f;           // 2^16: undoes the 2^-8 of both fp16 operands
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 static_assert(WAVES * 32 * 72 * 4 <= LDS_BYTES, "epilogue staging");

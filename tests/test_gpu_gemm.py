@@ -49,7 +49,8 @@ def _exact_regime_problem(fmt, M, N, K, seed, out):
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
 @pytest.mark.parametrize("out", ["bf16", "f16"])
-@pytest.mark.parametrize("shape", [(160, 96, 1024), (33, 272, 96), (256, 256, 2048)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(160, 96, 1024), (33, 272, 96), (256, 256, 2048), (384, 256, 512)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_exact_regime_bit_exact(fmt, out, shape):
     p = _exact_regime_problem(fmt, *shape, seed=sum(shape), out=out)
     D = run(p)
@@ -204,7 +205,8 @@ def test_plan_info():
 # NVFP4 small-M problems split K across workgroups (fp32 partials in the plan's workspace, summed in
 # split order by a second kernel); these shapes cover split and unsplit plans, ragged M / N and a
 # final half K tile (K % 64 == 32).
-NVFP4_SPLIT_SHAPES = [(100, 80, 1056), (1, 16, 4128), (129, 4000, 2080), (256, 1024, 2048), (640, 4096, 256)]
+NVFP4_SPLIT_SHAPES = [(100, 80, 1056), (1, 16, 4128), (129, 4000, 2080), (256, 1024, 2048), (640, 4096, 256),
+                      (512, 1024, 4096), (300, 2048, 1056)]
 
 
 @pytest.mark.parametrize("shape", NVFP4_SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -225,8 +227,27 @@ def test_nvfp4_split_k(shape, epi):
     assert rep["ok"], rep
 
 
+def _graph_replay_matches_eager(plan, problems):
+    """Replayed HIP graphs (every kernel of a call captured) give the eager bits, for each input set."""
+    devs, eager = [], []
+    for q in problems:
+        d = to_device(q)
+        eager.append(run(q, plan=plan, dev=d))
+        devs.append(d)
+    sets = []
+    for d, q in zip(devs, problems):
+        d["D"].fill_(0x7FFF)
+        sets.append(dict(A=d["A"], B=d["B"], sA=d["sA"], sB=d["sB"], D=d["D"], alpha=float(q["alpha"]),
+                         bias=d["bias"]))
+    stream = torch.cuda.Stream()
+    bsg.bench_loop(plan, sets, 3, 1, stream)
+    torch.cuda.synchronize()
+    for d, want in zip(devs, eager):
+        assert np.array_equal(d["D"].cpu().numpy().view(np.uint16), want)
+
+
 def test_nvfp4_split_k_deterministic_alpha_ptr_and_graph():
-    p = si.workload("nvfp4_256x4096x4096_loop")
+    p = si.problem("nvfp4", 256, 1024, 4096, seed=1234, bias=True, silu=True, out="bf16", alpha=0.3)
     plan = make_plan(p)
     assert plan.info()["workspace_bytes"] > 0
     dev = to_device(p)
@@ -235,27 +256,25 @@ def test_nvfp4_split_k_deterministic_alpha_ptr_and_graph():
     assert np.array_equal(D0, D1)
     alpha_dev = torch.tensor([float(p["alpha"])], dtype=torch.float32, device="cuda")
     dev["D"].fill_(0x7FFF)
-    plan.run_alpha_ptr(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha_dev)
+    plan.run_alpha_ptr(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha_dev, bias=dev["bias"])
     torch.cuda.synchronize()
     assert np.array_equal(dev["D"].cpu().numpy().view(np.uint16), D0)
-    # replayed HIP graphs (both kernels of a call captured) give the eager bits, for each of two sets
-    q = si.workload("nvfp4_256x4096x4096_loop", set_id=1)
-    devq = to_device(q)
-    Dq = run(q, plan=plan, dev=devq)
-    sets = []
-    for d, pp in ((dev, p), (devq, q)):
-        d["D"].fill_(0x7FFF)
-        sets.append(dict(A=d["A"], B=d["B"], sA=d["sA"], sB=d["sB"], D=d["D"], alpha=float(pp["alpha"])))
-    stream = torch.cuda.Stream()
-    bsg.bench_loop(plan, sets, 3, 1, stream)
-    torch.cuda.synchronize()
-    assert np.array_equal(dev["D"].cpu().numpy().view(np.uint16), D0)
-    assert np.array_equal(devq["D"].cpu().numpy().view(np.uint16), Dq)
+    q = si.problem("nvfp4", 256, 1024, 4096, seed=4321, bias=True, silu=True, out="bf16", alpha=0.3)
+    _graph_replay_matches_eager(plan, [p, q])
+
+
+def test_nvfp4_loop_workload_graph_replay():
+    p = si.workload("nvfp4_256x4096x4096_loop")
+    plan = make_plan(p)
+    _graph_replay_matches_eager(plan, [p, si.workload("nvfp4_256x4096x4096_loop", set_id=1)])
 
 
 def test_nvfp4_plan_info():
-    plan = bsg.Plan("nvfp4", 128, 8192, 8192, out="bf16", bias=True, silu=True)
-    info = plan.info()
-    assert info["variant"].startswith("nvfp4_")
+    # M <= 128: 128 x 256 tiles sharing the decoded A tile; the 32 tiles of 128 x 8192 split K
+    info = bsg.Plan("nvfp4", 128, 8192, 8192, out="bf16", bias=True, silu=True).info()
+    assert info["variant"].startswith("nvfp4_128x256_sharedA")
     splits = info["grid"][0] // (8192 // info["tile"][1])
     assert splits > 1 and info["workspace_bytes"] == splits * 128 * 8192 * 4
+    # larger M shares the decoded B tile; enough tiles to fill the chip run unsplit
+    info = bsg.Plan("nvfp4", 4096, 4096, 4096, out="f16").info()
+    assert info["variant"].startswith("nvfp4_256x128") and info["workspace_bytes"] == 0
