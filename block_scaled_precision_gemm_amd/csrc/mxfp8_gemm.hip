@@ -102,7 +102,7 @@ const KernelVariant kDirect[8] = {
 // for the remaining K % 32 == 0.
 const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K) {
   const int64_t large_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (K % 512 == 0 && large_tiles >= 256) return mxfp8_plr_variants();
+  if (K % 512 == 0 && large_tiles >= 256) return mxfp8_pp_variants();
   return K % 128 == 0 ? mxfp8_tiled_variants(M, N) : kDirect;
 }
 

@@ -1,0 +1,348 @@
+// MXFP8 block-scaled GEMM: 8-wave ping-pong kernel for gfx950 (K % 512 == 0, large M x N).
+//
+// Same operation as mxfp8_gemm.hip (E4M3 operands with one E8M0 scale per 32 K elements: the
+// mx_float8_t / float_ue8m0_t operands of the nvFuser PR #5736 page).
+//
+// * Workgroup tile 256 x 256, eight waves, two per SIMD.  Wave w = 4g + s (g = group, s = SIMD)
+//   owns rows 128g .. 128g+127 and columns 64s .. 64s+63 of the tile: 4 x 2 accumulators of
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (128 registers).
+// * Ping-pong: the two waves of a SIMD alternate between a memory phase (fragment reads of the next
+//   64-wide K slice from LDS, and copies) and a compute phase (its 8 MFMAs on one 64-wide K slice,
+//   512 cycles).  Group 1 starts one phase late, so in every phase one group computes while the
+//   other moves data, and one barrier per phase keeps them in step.  With a single wave per SIMD
+//   the copies, fragment reads and barriers could not overlap that wave's own MFMAs.
+// * Global -> LDS: K tiles of 128 bytes per row (64 KiB per 256 x 256 tile pair), two LDS stages,
+//   filled by buffer_load_dwordx4 ... lds with 8 lanes per 128-byte row piece.  Full 128-byte row
+//   pieces stream about 1.7x faster than 64-byte ones (measured in this access pattern), which is
+//   what lets the copies keep up with the MFMAs.  Group 0 issues the whole next K tile at the start
+//   of each K tile (16 instructions per wave), about 2048 cycles before it is read.
+// * E8M0 scales arrive every 512 K as 16 bytes per row (double-buffered, copied by group 1); the K
+//   loop is unrolled over those 512 K so stage offsets and wait counts are compile-time.  Copies
+//   past the last K tile use an offset beyond the buffer's range: zero-filled, no memory traffic.
+// * LDS rows are 128 bytes = 8 chunks of 16; chunk c of row R is stored at chunk c ^ ((R >> 1) & 7),
+//   which makes every 16-lane group of a fragment read hit 64 distinct banks.
+// * Epilogue: MFMA operands are swapped (B_j x A_i^T) so a lane's accumulators run along 4
+//   consecutive columns; values are finished in registers (alpha, bias, SiLU, rounding), staged in
+//   LDS and stored along rows, 16 bytes per lane.
+// * XCD-aware tile order as in mxfp8_plr.hip.
+//
+// Scaled-MFMA operand layout (measured on the device): lane l (r = l % 32, h = l / 32) holds K bytes
+// [16h, 16h+16) and [32+16h, 32+16h+16) of its row's 64-byte slice; its scale byte is the E8M0
+// code of 32-block h.
+#include <type_traits>
+
+#include "common.h"
+#include "epilogue.h"
+
+namespace bsg {
+namespace mxp {
+
+constexpr int BM = 256, BN = 256;
+constexpr int BK = 128;                          // K bytes per row per LDS stage
+constexpr int HK = 64;                           // K per phase (one MFMA K step)
+constexpr int NS = 2, UNROLL = 8;                // LDS stages; phases per 512 K (one scale batch)
+constexpr int WAVES = 8, THREADS = 64 * WAVES;
+constexpr int WROWS = 128, WCOLS = 64;           // a wave's block of D
+constexpr int TM = WROWS / 32, TN = WCOLS / 32;  // 4 x 2 MFMA tiles per wave
+constexpr int A_TILE = BM * BK, B_TILE = BN * BK;  // 32 KiB each; LDS: A stages, then B stages
+constexpr int B_BASE = NS * A_TILE;
+constexpr int SCALE_BYTES = 16;                                            // per row per 512 K
+constexpr int SCALE_BUF = (BM + BN) * SCALE_BYTES;                         // 8 KiB: A rows, B rows
+constexpr int MAIN_LDS = NS * (A_TILE + B_TILE) + 2 * SCALE_BUF;          // 144 KiB
+constexpr int EPI_ROW = 2 * WCOLS + 16, EPI_WAVE = WROWS * EPI_ROW;        // 64 cols + pad
+constexpr int LDS_BYTES = MAIN_LDS > WAVES * EPI_WAVE ? MAIN_LDS : WAVES * EPI_WAVE;
+constexpr int CPW = BM * BK / 1024 / 4;  // copy instructions per wave per K tile: 8
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+// An offset past any operand buffer (operands have < 2^31 bytes, so no 32-bit wrap): the load
+// returns zeros without touching memory.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+static_assert(CPW * 8 * 4 == BM && BM == BN, "copy split: 4 waves x 8 instructions x 8 rows");
+static_assert(4 * 64 == BM && 4 * 64 == BN, "scale split: 4 waves x 64 rows per operand");
+static_assert(TM == 4 && TN == 2, "the accumulator pin lists 4 x 2 tiles");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ v16f mfma_mx(v8i a, v8i b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
+  const int T = tiles_m * tiles_n;
+  int id = bid;
+  if ((T & 7) == 0) id = (bid & 7) * (T >> 3) + (bid >> 3);  // contiguous range per XCD
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = id / per_group;
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = id - group * per_group;
+  return make_int2(first_m + in_group % gsize, in_group / gsize);
+}
+
+// vmcnt wait with an LDS wait, then the barrier; the barrier alone.
+template <int N>
+__device__ __forceinline__ void phase_end() {
+  if constexpr (N < 0)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <Out O, bool BIAS, bool SILU>
+__global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  uint8_t* const scale_lds = lds + NS * (A_TILE + B_TILE);  // two buffers: [A rows][16], [B rows][16]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2, ws = wave & 3;
+  const int r = lane & 31, h = lane >> 5;
+  const int2 t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n);
+  const int m0 = t.x * BM, n0 = t.y * BN;
+  const int K = p.K, KB = K >> 5, KT = K / BK;  // K tiles of 128
+  const int m_valid = min(BM, p.M - m0), n_valid = min(BN, p.N - n0);
+
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (size_t)m0 * K), (short)0, m_valid * K, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (size_t)n0 * K), (short)0, n_valid * K, kRsrcWord3);
+  // group 0 copies A and sA, group 1 copies B and sB (every wave issues the same instruction mix:
+  // copies under a branch make the compiler drain them before LDS reads)
+  const __amdgpu_buffer_rsrc_t rsT = grp == 0 ? rsA : rsB;
+  const __amdgpu_buffer_rsrc_t rsS =
+      grp == 0
+          ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.sA + (size_t)m0 * KB), (short)0, m_valid * KB, kRsrcWord3)
+          : __builtin_amdgcn_make_buffer_rsrc((void*)(p.sB + (size_t)n0 * KB), (short)0, n_valid * KB, kRsrcWord3);
+
+  // Copy plan: a K tile of an operand is 256 rows x 128 bytes = 32 instructions of 8 rows; wave
+  // 4g + s issues instructions 8s .. 8s+7 of operand g.  Lane j writes LDS bytes [16j, 16j+16) of
+  // the instruction's KiB: row R = 8*ins + j/8, physical chunk j%8, holding logical chunk
+  // (j%8) ^ swz(R), so the 8 lanes of a row read its whole 128-byte piece.
+  // Instruction q covers rows 64s + 8q .. +7; swz(R) = (4q + lane / 16) & 7 depends on q only through
+  // its parity, so the lane part of the offset takes two values and 8qK goes to the scalar offset.
+  uint32_t voff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int R = 8 * (CPW * ws + par) + (lane >> 3);
+    voff[par] = (uint32_t)(R - 8 * par) * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz(R));
+  }
+  uint8_t* const copy_dst = lds + grp * B_BASE + CPW * ws * 1024;
+  // Scale plan: wave 4g + s copies rows 64s .. 64s+63 of operand g's scales, 16 bytes each.
+  const uint32_t soff = (uint32_t)(64 * ws + lane) * (uint32_t)KB;
+  uint8_t* const sdst = scale_lds + grp * BM * SCALE_BYTES + 64 * ws * SCALE_BYTES;
+
+  auto copy_tile = [&](auto sc, int kt) {
+    constexpr int stage = decltype(sc)::value;
+    static_assert(A_TILE == B_TILE, "one stage stride for both operands");
+    uint8_t* dst = copy_dst + stage * A_TILE;
+    const uint32_t k0 = kt < KT ? (uint32_t)kt * BK : kOutOfRange;
+#pragma unroll
+    for (int q = 0; q < CPW; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, (lds_void*)(dst + q * 1024), 16, voff[q & 1],
+                                               k0 + (uint32_t)(8 * q) * (uint32_t)K, 0, 0);
+  };
+  auto copy_scales = [&](auto bc, int batch) {
+    constexpr int buf = decltype(bc)::value;
+    const uint32_t k0 = batch < KT * BK / 512 ? (uint32_t)batch * SCALE_BYTES : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, (lds_void*)(sdst + buf * SCALE_BUF), 16, soff, k0, 0, 0);
+  };
+
+  // per-lane LDS offsets of the fragment chunks h and 2 + h of the first 64-byte half of a row
+  // (rows 32i + r share r's swizzle); the second half uses chunks 4 + h and 6 + h
+  const int f = swz(r);
+  const int off00 = 16 * (h ^ f), off01 = 16 * ((2 + h) ^ f);
+  const int off10 = 16 * ((4 + h) ^ f), off11 = 16 * ((6 + h) ^ f);
+  const int a_row = (WROWS * grp + r) * BK;
+  const int b_row = (WCOLS * ws + r) * BK;
+
+  v8i af[TM], bf[TN];
+  uint32_t sa[TM][4], sb[TN][4];  // 16 scale bytes per row-tile for the current 512 K
+
+  auto read_frags = [&](auto sc, auto hc) {
+    constexpr int stage = decltype(sc)::value;
+    constexpr int half = decltype(hc)::value;
+    const int o0 = half ? off10 : off00, o1 = half ? off11 : off01;
+    const uint8_t* a_lds = lds + stage * A_TILE;
+    const uint8_t* b_lds = lds + B_BASE + stage * B_TILE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint8_t* pa = a_lds + a_row + i * 32 * BK;
+      const v4i x0 = *(const v4i*)(pa + o0), x1 = *(const v4i*)(pa + o1);
+      af[i] = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const uint8_t* pb = b_lds + b_row + j * 32 * BK;
+      const v4i x0 = *(const v4i*)(pb + o0), x1 = *(const v4i*)(pb + o1);
+      bf[j] = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    }
+  };
+  auto read_scales = [&](auto bc) {
+    constexpr int buf = decltype(bc)::value;
+    const uint8_t* s = scale_lds + buf * SCALE_BUF;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const v4i v = *(const v4i*)(s + (WROWS * grp + 32 * i + r) * SCALE_BYTES);
+      sa[i][0] = v[0]; sa[i][1] = v[1]; sa[i][2] = v[2]; sa[i][3] = v[3];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const v4i v = *(const v4i*)(s + BM * SCALE_BYTES + (WCOLS * ws + 32 * j + r) * SCALE_BYTES);
+      sb[j][0] = v[0]; sb[j][1] = v[1]; sb[j][2] = v[2]; sb[j][3] = v[3];
+    }
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (v16f){};
+
+  // Prologue: K tile 0 and the scales of the first 512 K become visible at the barrier.  Group 1 then
+  // waits one phase.
+  copy_tile(std::integral_constant<int, 0>{}, 0);
+  copy_scales(std::integral_constant<int, 0>{}, 0);
+  phase_end<0>();
+  if (grp == 1) barrier_only();
+
+  // Phase u (0..7) of a 512-K batch works on K slice kb + 64u: K tile (kb + 64u) / 128 in stage
+  // (u / 2) % 2, half u % 2.  In the memory phase of every even u each wave issues its share of the
+  // next K tile; at u == 1 its share of the next batch's scales.  Each wave waits for its tile share
+  // before the barrier that ends global phase 2h + 3 (h = global index of the even slice): group 0
+  // at the end of its compute phase of u + 1, group 1 at the end of its memory phase of u + 1.  No
+  // wave reads that stage before then.  The scale share is waited for by u == 3 in the same way.
+  int kb = 0;  // in 64-wide K slices
+  auto step = [&](auto uc, auto bc) {
+    constexpr int u = decltype(uc)::value;
+    constexpr int buf = decltype(bc)::value;  // scale buffer of this batch
+    constexpr int stage = (u >> 1) & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (u == 0) read_scales(bc);
+    read_frags(std::integral_constant<int, stage>{}, std::integral_constant<int, u & 1>{});
+    if constexpr ((u & 1) == 0) copy_tile(std::integral_constant<int, stage ^ 1>{}, (kb + u) / 2 + 1);
+    if constexpr (u == 1) copy_scales(std::integral_constant<int, buf ^ 1>{}, kb / UNROLL + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (u & 1) {
+      if (grp == 1)
+        phase_end<u == 1 ? 1 : 0>();  // the tile share copied at u - 1 (the scales may stay in flight)
+      else
+        phase_end<-1>();
+    } else {
+      phase_end<-1>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // this slice's scale operands (byte 2u + h of the batch's 16 is in dword u/2)
+    const int shift = 8 * (2 * (u & 1) + h);
+    int ssa[TM], ssb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ssa[i] = (int)(sa[i][u >> 1] >> shift);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) ssb[j] = (int)(sb[j][u >> 1] >> shift);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(bf[j], af[i], acc[i][j], ssb[j], ssa[i]);
+    // The MFMAs have no memory effects; this empty asm that reads their results keeps them inside
+    // this phase (otherwise they can sink past the group-dependent barrier branches below).
+    asm volatile("" ::"v"(acc[0][0]), "v"(acc[0][1]), "v"(acc[1][0]), "v"(acc[1][1]), "v"(acc[2][0]),
+                 "v"(acc[2][1]), "v"(acc[3][0]), "v"(acc[3][1]));
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (u & 1) {
+      if (grp == 0)
+        phase_end<u == 1 ? 1 : 0>();  // the tile share copied at u - 1 (the scales may stay in flight)
+      else
+        barrier_only();
+    } else {
+      barrier_only();
+    }
+  };
+  auto batch = [&](auto bc) {
+    step(std::integral_constant<int, 0>{}, bc);
+    step(std::integral_constant<int, 1>{}, bc);
+    step(std::integral_constant<int, 2>{}, bc);
+    step(std::integral_constant<int, 3>{}, bc);
+    step(std::integral_constant<int, 4>{}, bc);
+    step(std::integral_constant<int, 5>{}, bc);
+    step(std::integral_constant<int, 6>{}, bc);
+    step(std::integral_constant<int, 7>{}, bc);
+    kb += UNROLL;
+  };
+  const int KS = K / HK;  // 64-wide K slices, a multiple of 8
+  for (; kb + 2 * UNROLL <= KS;) {
+    batch(std::integral_constant<int, 0>{});
+    batch(std::integral_constant<int, 1>{});
+  }
+  if (kb < KS) batch(std::integral_constant<int, 0>{});
+
+  // Epilogue.  Group 0 catches up with group 1's last compute phase; then every wave has drained
+  // its copies and LDS reads before the stages are reused for staging.
+  // acc[i][j] holds rows 32i.., columns 32j.. of the wave's 128 x 64 block, transposed: lane (r, h),
+  // element 4g + c is row r, column 8g + 4h + c.
+  __builtin_amdgcn_sched_barrier(0);
+  if (grp == 0) barrier_only();
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const float alpha = load_alpha(p);
+  uint8_t* const eb = lds + wave * EPI_WAVE;
+  const int nw = n0 + WCOLS * ws;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c0 = 32 * j + 8 * g + 4 * h;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BIAS) {
+        if (nw + c0 < p.N) {
+          const v4f b4 = *(const v4f*)(p.bias + nw + c0);
+          bv[0] = b4[0]; bv[1] = b4[1]; bv[2] = b4[2]; bv[3] = b4[3];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const v16f& a = acc[i][j];
+        const uint32_t lo = pack2_out<O>(epi_value<SILU>(a[4 * g + 0], alpha, bv[0]),
+                                         epi_value<SILU>(a[4 * g + 1], alpha, bv[1]));
+        const uint32_t hi = pack2_out<O>(epi_value<SILU>(a[4 * g + 2], alpha, bv[2]),
+                                         epi_value<SILU>(a[4 * g + 3], alpha, bv[3]));
+        *(uint2*)(eb + (32 * i + r) * EPI_ROW + 2 * c0) = make_uint2(lo, hi);
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the block is private to this wave
+  uint16_t* D = (uint16_t*)p.D;
+  const int mw = m0 + WROWS * grp;
+  const int cc = 8 * (lane & 7);  // this lane's 8 columns; 8 lanes per 128-byte row
+#pragma unroll
+  for (int q = 0; q < WROWS / 8; ++q) {
+    const int row = 8 * q + (lane >> 3);
+    const v4i v = *(const v4i*)(eb + row * EPI_ROW + 2 * cc);
+    const int m = mw + row, n = nw + cc;
+    if (m < p.M && n < p.N) *(v4i*)(D + (size_t)m * p.N + n) = v;
+  }
+}
+
+template <Out O, bool BIAS, bool SILU>
+hipError_t launch_pp(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
+  void* kargs[] = {(void*)&args};
+  return hipLaunchKernel((const void*)&mxfp8_pp_kernel<O, BIAS, SILU>, grid, block, kargs, 0, stream);
+}
+
+#define BSG_MX_PP(O, B, S) \
+  { "mxfp8_pp_256x256x64_w8", &launch_pp<O, B, S>, BM, BN, BK, THREADS, (uint32_t)LDS_BYTES, true }
+const KernelVariant kPp[8] = {
+    BSG_MX_PP(Out::BF16, false, false), BSG_MX_PP(Out::BF16, false, true),
+    BSG_MX_PP(Out::BF16, true, false),  BSG_MX_PP(Out::BF16, true, true),
+    BSG_MX_PP(Out::F16, false, false),  BSG_MX_PP(Out::F16, false, true),
+    BSG_MX_PP(Out::F16, true, false),   BSG_MX_PP(Out::F16, true, true),
+};
+#undef BSG_MX_PP
+
+}  // namespace mxp
+
+const KernelVariant* mxfp8_pp_variants() { return mxp::kPp; }
+
+}  // namespace bsg
