@@ -34,8 +34,8 @@ HBM_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "mxfp8_4096_counters.json")
 
 
-# Sources of the headline kernel (mxfp8_plr): committed counters are valid only for these bytes.
-HEADLINE_SOURCES = ("mxfp8_plr.hip", "common.h", "epilogue.h")
+# Sources of the headline kernel (mxfp8_pp): committed counters are valid only for these bytes.
+HEADLINE_SOURCES = ("mxfp8_pp.hip", "common.h", "epilogue.h")
 
 
 def kernel_source_hash() -> str:
@@ -62,7 +62,7 @@ def write_counters(fetch_csv: str, write_csv: str) -> int:
         return {k: statistics.mean(v) for k, v in vals.items()}
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    gemm = [k for k in fetch if "mxfp8_plr_kernel" in k]
+    gemm = [k for k in fetch if "mxfp8_pp_kernel" in k]
     copy = [k for k in fetch if "copyBuffer" in k]
     if len(gemm) != 1 or len(copy) != 1:
         print(f"expected one GEMM and one copy kernel, got {list(fetch)}", file=sys.stderr)
@@ -203,8 +203,8 @@ def traffic_from_counters(gpu_ms: float) -> dict | None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--only-main", action="store_true", help="time the headline workload only (for profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run a device copy of known size (HBM counter calibration)")
@@ -243,10 +243,12 @@ def main() -> int:
 
     extra = {}
     if not args.only_main:
-        for name, steps in (("mxfp8_8192_silu", 20), ("nvfp4_128x8192x8192_silu", 100), ("mxfp8_256", 500)):
+        # warm-up lengths cover the clock / power transient of the first few hundred calls
+        for name, steps, warm in (("mxfp8_8192_silu", 30, 60), ("nvfp4_128x8192x8192_silu", 200, 400),
+                                  ("mxfp8_256", 500, 500)):
             log(f"workload {name}")
             q = si.workload(name)
-            r = time_gemm(q, steps, max(5, steps // 5), stream)
+            r = time_gemm(q, steps, warm, stream)
             peak = PEAK_TFLOPS["mxfp8"] if q["fmt"] == "mxfp8" else PEAK_TFLOPS["nvfp4_fp4"]
             r["frac_of_mx_peak"] = r["tflops_gpu"] / peak
             if q["fmt"] == "nvfp4":

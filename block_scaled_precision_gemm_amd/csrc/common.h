@@ -50,8 +50,6 @@ struct KernelVariant {
 // Each kernel family returns its table for the M bucket it serves.
 const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K);
 const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N);
-const KernelVariant* mxfp8_pipe_variants();
-const KernelVariant* mxfp8_plr_variants();
 const KernelVariant* mxfp8_pp_variants();
 const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K);
 

@@ -14,17 +14,21 @@
 // * Global -> LDS: K tiles of 128 bytes per row (64 KiB per 256 x 256 tile pair), two LDS stages,
 //   filled by buffer_load_dwordx4 ... lds with 8 lanes per 128-byte row piece.  Full 128-byte row
 //   pieces stream about 1.7x faster than 64-byte ones (measured in this access pattern), which is
-//   what lets the copies keep up with the MFMAs.  Group 0 issues the whole next K tile at the start
-//   of each K tile (16 instructions per wave), about 2048 cycles before it is read.
-// * E8M0 scales arrive every 512 K as 16 bytes per row (double-buffered, copied by group 1); the K
-//   loop is unrolled over those 512 K so stage offsets and wait counts are compile-time.  Copies
-//   past the last K tile use an offset beyond the buffer's range: zero-filled, no memory traffic.
+//   what lets the copies keep up with the MFMAs.  Every memory phase issues one quarter of the next
+//   K tile (4 instructions per wave), so the address work of the copies is spread evenly: issuing a
+//   whole tile in one phase held that phase's memory waves back.
+// * E8M0 scales arrive every 512 K as 16 bytes per row (double-buffered; A's copied by group 0, B's
+//   by group 1); the K loop is unrolled over those 512 K so stage offsets and wait counts are
+//   compile-time.  Copies past the last K tile use an offset beyond the buffer's range: zero-filled,
+//   no memory traffic.
 // * LDS rows are 128 bytes = 8 chunks of 16; chunk c of row R is stored at chunk c ^ ((R >> 1) & 7),
 //   which makes every 16-lane group of a fragment read hit 64 distinct banks.
 // * Epilogue: MFMA operands are swapped (B_j x A_i^T) so a lane's accumulators run along 4
 //   consecutive columns; values are finished in registers (alpha, bias, SiLU, rounding), staged in
 //   LDS and stored along rows, 16 bytes per lane.
-// * XCD-aware tile order as in mxfp8_plr.hip.
+// * XCD-aware tile order: workgroups go to the 8 XCDs round-robin, so each XCD gets a contiguous
+//   range of tile ids, walked in groups of 8 tile-rows; the tiles an XCD runs at once share A and B
+//   panels in its L2.
 //
 // Scaled-MFMA operand layout (measured on the device): lane l (r = l % 32, h = l / 32) holds K bytes
 // [16h, 16h+16) and [32+16h, 32+16h+16) of its row's 64-byte slice; its scale byte is the E8M0
@@ -51,13 +55,13 @@ constexpr int SCALE_BUF = (BM + BN) * SCALE_BYTES;                         // 8 
 constexpr int MAIN_LDS = NS * (A_TILE + B_TILE) + 2 * SCALE_BUF;          // 144 KiB
 constexpr int EPI_ROW = 2 * WCOLS + 16, EPI_WAVE = WROWS * EPI_ROW;        // 64 cols + pad
 constexpr int LDS_BYTES = MAIN_LDS > WAVES * EPI_WAVE ? MAIN_LDS : WAVES * EPI_WAVE;
-constexpr int CPW = BM * BK / 1024 / 4;  // copy instructions per wave per K tile: 8
+constexpr int CPW = BM * BK / 1024 / 8;  // copy instructions per wave per 64-wide K slice: 4
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 // An offset past any operand buffer (operands have < 2^31 bytes, so no 32-bit wrap): the load
 // returns zeros without touching memory.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-static_assert(CPW * 8 * 4 == BM && BM == BN, "copy split: 4 waves x 8 instructions x 8 rows");
+static_assert(CPW * 8 * 4 * 2 == BM && BM == BN, "copy split: 2 row halves x 4 waves x 4 instructions x 8 rows");
 static_assert(4 * 64 == BM && 4 * 64 == BN, "scale split: 4 waves x 64 rows per operand");
 static_assert(TM == 4 && TN == 2, "the accumulator pin lists 4 x 2 tiles");
 
@@ -111,39 +115,45 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (size_t)m0 * K), (short)0, m_valid * K, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rsB =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (size_t)n0 * K), (short)0, n_valid * K, kRsrcWord3);
-  // group 0 copies A and sA, group 1 copies B and sB (every wave issues the same instruction mix:
-  // copies under a branch make the compiler drain them before LDS reads)
-  const __amdgpu_buffer_rsrc_t rsT = grp == 0 ? rsA : rsB;
+  // Copies of K tile k+1 are spread over the four memory phases of K tile k (slices u even / odd of
+  // group 0 / group 1), one quarter each: operand g ^ (u & 1), rows 128 (u & 1) .. +127.  So group 0
+  // copies A rows 0..127 (even u) and B rows 128..255 (odd u), group 1 B rows 0..127 and A rows
+  // 128..255.  Every wave issues the same instruction mix (copies under a branch make the compiler
+  // drain them before LDS reads); group 0 copies A's scales, group 1 B's.
+  const __amdgpu_buffer_rsrc_t rsT0 = grp == 0 ? rsA : rsB, rsT1 = grp == 0 ? rsB : rsA;
   const __amdgpu_buffer_rsrc_t rsS =
       grp == 0
           ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.sA + (size_t)m0 * KB), (short)0, m_valid * KB, kRsrcWord3)
           : __builtin_amdgcn_make_buffer_rsrc((void*)(p.sB + (size_t)n0 * KB), (short)0, n_valid * KB, kRsrcWord3);
 
-  // Copy plan: a K tile of an operand is 256 rows x 128 bytes = 32 instructions of 8 rows; wave
-  // 4g + s issues instructions 8s .. 8s+7 of operand g.  Lane j writes LDS bytes [16j, 16j+16) of
-  // the instruction's KiB: row R = 8*ins + j/8, physical chunk j%8, holding logical chunk
-  // (j%8) ^ swz(R), so the 8 lanes of a row read its whole 128-byte piece.
-  // Instruction q covers rows 64s + 8q .. +7; swz(R) = (4q + lane / 16) & 7 depends on q only through
-  // its parity, so the lane part of the offset takes two values and 8qK goes to the scalar offset.
+  // Copy plan: a quarter is 128 rows x 128 bytes = 16 instructions of 8 rows; wave 4g + s issues
+  // instructions 4s .. 4s+3 (rows 32s + 8q .. +7 of the half).  Lane j writes LDS bytes
+  // [16j, 16j+16) of the instruction's KiB: row R = 8*ins + j/8, physical chunk j%8, holding logical
+  // chunk (j%8) ^ swz(R), so the 8 lanes of a row read its whole 128-byte piece.  swz(R) =
+  // (4q + lane / 16) & 7 depends on q only through its parity, so the lane part of the offset takes
+  // two values; the row part (128 half + 8q) K goes to the scalar offset.
   uint32_t voff[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int R = 8 * (CPW * ws + par) + (lane >> 3);
-    voff[par] = (uint32_t)(R - 8 * par) * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz(R));
+  for (int qp = 0; qp < 2; ++qp) {
+    const int R = 32 * ws + 8 * qp + (lane >> 3);
+    voff[qp] = (uint32_t)(R - 8 * qp) * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz(R));
   }
-  uint8_t* const copy_dst = lds + grp * B_BASE + CPW * ws * 1024;
+  uint8_t* const copy_dst0 = lds + grp * B_BASE + CPW * ws * 1024;              // operand g, rows 0..127
+  uint8_t* const copy_dst1 = lds + (1 - grp) * B_BASE + (16 + CPW * ws) * 1024;  // the other, 128..255
   // Scale plan: wave 4g + s copies rows 64s .. 64s+63 of operand g's scales, 16 bytes each.
   const uint32_t soff = (uint32_t)(64 * ws + lane) * (uint32_t)KB;
   uint8_t* const sdst = scale_lds + grp * BM * SCALE_BYTES + 64 * ws * SCALE_BYTES;
 
-  auto copy_tile = [&](auto sc, int kt) {
+  auto copy_quarter = [&](auto sc, auto pc, int kt) {
     constexpr int stage = decltype(sc)::value;
+    constexpr int par = decltype(pc)::value;
     static_assert(A_TILE == B_TILE, "one stage stride for both operands");
-    uint8_t* dst = copy_dst + stage * A_TILE;
-    const uint32_t k0 = kt < KT ? (uint32_t)kt * BK : kOutOfRange;
+    uint8_t* dst = (par ? copy_dst1 : copy_dst0) + stage * A_TILE;
+    const __amdgpu_buffer_rsrc_t rs = par ? rsT1 : rsT0;
+    const uint32_t k0 = kt < KT ? (uint32_t)kt * BK + (uint32_t)(128 * par) * (uint32_t)K : kOutOfRange;
 #pragma unroll
     for (int q = 0; q < CPW; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsT, (lds_void*)(dst + q * 1024), 16, voff[q & 1],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + q * 1024), 16, voff[q & 1],
                                                k0 + (uint32_t)(8 * q) * (uint32_t)K, 0, 0);
   };
   auto copy_scales = [&](auto bc, int batch) {
@@ -205,17 +215,20 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
 
   // Prologue: K tile 0 and the scales of the first 512 K become visible at the barrier.  Group 1 then
   // waits one phase.
-  copy_tile(std::integral_constant<int, 0>{}, 0);
+  copy_quarter(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, 0);
+  copy_quarter(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, 0);
   copy_scales(std::integral_constant<int, 0>{}, 0);
   phase_end<0>();
   if (grp == 1) barrier_only();
 
   // Phase u (0..7) of a 512-K batch works on K slice kb + 64u: K tile (kb + 64u) / 128 in stage
-  // (u / 2) % 2, half u % 2.  In the memory phase of every even u each wave issues its share of the
-  // next K tile; at u == 1 its share of the next batch's scales.  Each wave waits for its tile share
-  // before the barrier that ends global phase 2h + 3 (h = global index of the even slice): group 0
-  // at the end of its compute phase of u + 1, group 1 at the end of its memory phase of u + 1.  No
-  // wave reads that stage before then.  The scale share is waited for by u == 3 in the same way.
+  // (u / 2) % 2, half u % 2.  With global phases 2h .. 2h+3 for the memory / compute phases of
+  // slices 2t and 2t+1 (group 0 at 2h, 2h+2; group 1 at 2h+1, 2h+3), group 0 reads the next K tile
+  // at 2h+4 and group 1 at 2h+5; A rows 128..255 are read only by group 1.  Waits (before the barrier
+  // that ends a phase): group 0 drains its copies at the end of its compute phase of odd u (2h+3);
+  // group 1 drains its even-u quarter at the end of its memory phase of odd u (2h+3) and everything
+  // at the end of its compute phase of odd u (2h+4).  The scale share, issued at u == 1 with the
+  // odd quarter, is drained with it.
   int kb = 0;  // in 64-wide K slices
   auto step = [&](auto uc, auto bc) {
     constexpr int u = decltype(uc)::value;
@@ -224,12 +237,12 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (u == 0) read_scales(bc);
     read_frags(std::integral_constant<int, stage>{}, std::integral_constant<int, u & 1>{});
-    if constexpr ((u & 1) == 0) copy_tile(std::integral_constant<int, stage ^ 1>{}, (kb + u) / 2 + 1);
+    copy_quarter(std::integral_constant<int, stage ^ 1>{}, std::integral_constant<int, u & 1>{}, (kb + u) / 2 + 1);
     if constexpr (u == 1) copy_scales(std::integral_constant<int, buf ^ 1>{}, kb / UNROLL + 1);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (u & 1) {
       if (grp == 1)
-        phase_end<u == 1 ? 1 : 0>();  // the tile share copied at u - 1 (the scales may stay in flight)
+        phase_end<CPW + (u == 1 ? 1 : 0)>();  // the quarter copied at u - 1
       else
         phase_end<-1>();
     } else {
@@ -252,14 +265,10 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
     asm volatile("" ::"v"(acc[0][0]), "v"(acc[0][1]), "v"(acc[1][0]), "v"(acc[1][1]), "v"(acc[2][0]),
                  "v"(acc[2][1]), "v"(acc[3][0]), "v"(acc[3][1]));
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (u & 1) {
-      if (grp == 0)
-        phase_end<u == 1 ? 1 : 0>();  // the tile share copied at u - 1 (the scales may stay in flight)
-      else
-        barrier_only();
-    } else {
+    if constexpr (u & 1)
+      phase_end<0>();  // both quarters (and at u == 1 the scales)
+    else
       barrier_only();
-    }
   };
   auto batch = [&](auto bc) {
     step(std::integral_constant<int, 0>{}, bc);

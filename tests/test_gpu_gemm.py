@@ -80,6 +80,49 @@ def test_epilogue_variants(fmt, bias, silu, out):
     _check(si.problem(fmt, 192, 160, 256, seed=300, bias=bias, silu=silu, out=out, alpha=0.5))
 
 
+def _band_rows(M, extra=()):
+    """Two rows in every 256-row band (one per 128-row half, at varying offsets) plus `extra`."""
+    rows = [r for b in range(0, M, 256) for r in (b + (37 * b // 256) % 128, b + 128 + (53 * b // 256) % 128)]
+    return np.unique(np.array([r for r in rows if r < M] + list(extra)))
+
+
+def _full_coverage(D):
+    """Every entry was written (the poison fill is a NaN pattern that finite inputs cannot produce)."""
+    assert not (D == 0x7FFF).any(), f"{int((D == 0x7FFF).sum())} entries of D were never written"
+
+
+# Large-shape MXFP8 kernel (>= 256 tiles of 256 x 256, K % 512 == 0): bit-exact in the exact regime,
+# including the banded tile order (M a multiple of 2048, N of 8192), and a ragged shape.
+@pytest.mark.parametrize("shape", [(4096, 4096, 512), (2048, 8192, 1024)], ids=lambda s: "x".join(map(str, s)))
+def test_large_mxfp8_exact_regime_bit_exact(shape):
+    M, N, K = shape
+    p = _exact_regime_problem("mxfp8", M, N, K, seed=M + K, out="bf16")
+    plan = make_plan(p)
+    assert plan.info()["variant"].startswith("mxfp8_pp"), plan.info()
+    D = run(p, plan=plan)
+    _full_coverage(D)
+    rows = _band_rows(M, extra=(M - 1,))
+    R = reference(p, rows=rows)["bits"]
+    assert np.array_equal(D[rows], R), f"{int((D[rows] != R).sum())} of {R.size} sampled entries differ"
+
+
+@pytest.mark.parametrize("shape,epi", [((4000, 4112, 1024), dict(out="bf16", alpha=0.5)),
+                                       ((2048, 8192, 512), dict(out="f16", bias=True, silu=True, alpha=0.25))],
+                         ids=["ragged", "band_bias_silu"])
+def test_large_mxfp8_sampled(shape, epi):
+    M, N, K = shape
+    p = si.problem("mxfp8", M, N, K, seed=K + 11, **epi)
+    plan = make_plan(p)
+    assert plan.info()["variant"].startswith("mxfp8_pp"), plan.info()
+    D = run(p, plan=plan)
+    _full_coverage(D)
+    rows = _band_rows(M, extra=(M - 2, M - 1))
+    ref = reference(p, rows=rows)
+    rep = compare(D[rows], ref, p["alpha"], p["silu"], p["out"])
+    print(f"[parity] mxfp8 {M}x{N}x{K} sampled {len(rows)} rows max_rel={rep['max_rel_err']:.3g}", flush=True)
+    assert rep["ok"], rep
+
+
 def test_config_mxfp8_256():
     _check(si.workload("mxfp8_256"))
 
