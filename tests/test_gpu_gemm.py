@@ -86,6 +86,11 @@ def _band_rows(M, extra=()):
     return np.unique(np.array([r for r in rows if r < M] + list(extra)))
 
 
+def _is_large_kernel(info):
+    """The large-shape MXFP8 kernel: 256 x 256 tiles, eight waves."""
+    return info["variant"].startswith("mxfp8_") and info["tile"][:2] == (256, 256) and info["block"] == 512
+
+
 def _full_coverage(D):
     """Every entry was written (the poison fill is a NaN pattern that finite inputs cannot produce)."""
     assert not (D == 0x7FFF).any(), f"{int((D == 0x7FFF).sum())} entries of D were never written"
@@ -98,7 +103,7 @@ def test_large_mxfp8_exact_regime_bit_exact(shape):
     M, N, K = shape
     p = _exact_regime_problem("mxfp8", M, N, K, seed=M + K, out="bf16")
     plan = make_plan(p)
-    assert plan.info()["variant"].startswith("mxfp8_pp"), plan.info()
+    assert _is_large_kernel(plan.info()), plan.info()
     D = run(p, plan=plan)
     _full_coverage(D)
     rows = _band_rows(M, extra=(M - 1,))
@@ -113,7 +118,7 @@ def test_large_mxfp8_sampled(shape, epi):
     M, N, K = shape
     p = si.problem("mxfp8", M, N, K, seed=K + 11, **epi)
     plan = make_plan(p)
-    assert plan.info()["variant"].startswith("mxfp8_pp"), plan.info()
+    assert _is_large_kernel(plan.info()), plan.info()
     D = run(p, plan=plan)
     _full_coverage(D)
     rows = _band_rows(M, extra=(M - 2, M - 1))
