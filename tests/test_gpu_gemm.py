@@ -87,8 +87,8 @@ def _band_rows(M, extra=()):
 
 
 def _is_large_kernel(info):
-    """The large-shape MXFP8 kernel: 256 x 256 tiles, eight waves."""
-    return info["variant"].startswith("mxfp8_") and info["tile"][:2] == (256, 256) and info["block"] == 512
+    """The large-shape MXFP8 kernel (K % 512 == 0, 256 x 256 tiles)."""
+    return info["variant"].startswith("mxfp8_pp") and info["tile"][:2] == (256, 256)
 
 
 def _full_coverage(D):
