@@ -69,8 +69,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// Scaled MFMA; SEL picks byte SEL of each 32-bit scale operand.
+template <int SEL>
 __device__ __forceinline__ v16f mfma_mx(v8i a, v8i b, v16f c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
 }
 
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
@@ -192,18 +194,22 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
       bf[j] = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
   };
+  // Dword d of a row's 16 scale bytes holds the 32-blocks of K tile d of the batch; shifted right by
+  // 8h, slice 2d + e finds the byte of its block h at byte 2e, which the MFMA selects itself (no
+  // per-slice shifts ahead of the MFMAs).
   auto read_scales = [&](auto bc) {
     constexpr int buf = decltype(bc)::value;
     const uint8_t* s = scale_lds + buf * SCALE_BUF;
+    const int hs = 8 * h;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const v4i v = *(const v4i*)(s + (WROWS * grp + 32 * i + r) * SCALE_BYTES);
-      sa[i][0] = v[0]; sa[i][1] = v[1]; sa[i][2] = v[2]; sa[i][3] = v[3];
+      sa[i][0] = v[0] >> hs; sa[i][1] = v[1] >> hs; sa[i][2] = v[2] >> hs; sa[i][3] = v[3] >> hs;
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const v4i v = *(const v4i*)(s + BM * SCALE_BYTES + (WCOLS * ws + 32 * j + r) * SCALE_BYTES);
-      sb[j][0] = v[0]; sb[j][1] = v[1]; sb[j][2] = v[2]; sb[j][3] = v[3];
+      sb[j][0] = v[0] >> hs; sb[j][1] = v[1] >> hs; sb[j][2] = v[2] >> hs; sb[j][3] = v[3] >> hs;
     }
   };
 
@@ -249,17 +255,11 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
       phase_end<-1>();
     }
     __builtin_amdgcn_sched_barrier(0);
-    // this slice's scale operands (byte 2u + h of the batch's 16 is in dword u/2)
-    const int shift = 8 * (2 * (u & 1) + h);
-    int ssa[TM], ssb[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) ssa[i] = (int)(sa[i][u >> 1] >> shift);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) ssb[j] = (int)(sb[j][u >> 1] >> shift);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(bf[j], af[i], acc[i][j], ssb[j], ssa[i]);
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = mfma_mx<2 * (u & 1)>(bf[j], af[i], acc[i][j], (int)sb[j][u >> 1], (int)sa[i][u >> 1]);
     // The MFMAs have no memory effects; this empty asm that reads their results keeps them inside
     // this phase (otherwise they can sink past the group-dependent barrier branches below).
     asm volatile("" ::"v"(acc[0][0]), "v"(acc[0][1]), "v"(acc[1][0]), "v"(acc[1][1]), "v"(acc[2][0]),
