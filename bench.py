@@ -15,6 +15,7 @@ of rows of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-main] [--calibration-copy]
        python bench.py --counters-from FETCH_CSV WRITE_CSV   (records HBM traffic from rocprofv3 passes)
+       python bench.py --api-loop N   (N direct calls per workload only, for rocprofv3 --hip-trace)
 """
 from __future__ import annotations
 
@@ -168,6 +169,25 @@ def loop_bench(stream, n_sets: int = 10, calls: int = 100) -> dict:
                 tflops_gpu=flops / (gpu_us * 1e-6) / 1e12)
 
 
+def api_loop(n: int, stream) -> int:
+    """N direct calls per workload from the native loop and nothing else timed: run twice under
+    `rocprofv3 --hip-trace --stats` with different N, the difference of the HIP API call counts is
+    what N calls of bsg_run cost (setup, uploads and plan creation cancel)."""
+    import torch
+    import block_scaled_precision_gemm_amd as bsg
+    import seeded_inputs as si
+    for name in ("nvfp4_256x4096x4096_loop", "mxfp8_4096"):
+        p = si.workload(name)
+        plan = bsg.Plan(p["fmt"], p["M"], p["N"], p["K"], out=p["out"], bias=p["bias"] is not None, silu=p["silu"])
+        d = device_inputs(p)
+        d["alpha"] = float(p["alpha"])
+        torch.cuda.synchronize()
+        us = bsg.bench_loop(plan, [d], n, 0, stream)
+        log(f"api loop {name}: {n} calls, {us / n:.2f} us per call, variant {plan.info()['variant']}")
+        plan.close()
+    return 0
+
+
 def cpu_baseline(p: dict, budget_s: float = 12.0) -> dict:
     """The oracle as it stands, timed on host cores over row chunks of the workload until the budget."""
     import numpy as np
@@ -208,6 +228,9 @@ def main() -> int:
     ap.add_argument("--only-main", action="store_true", help="time the headline workload only (for profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run a device copy of known size (HBM counter calibration)")
+    ap.add_argument("--api-loop", type=int, metavar="N",
+                    help="only run N direct bsg_run calls per workload (NVFP4 256x4096x4096 split-K, MXFP8 "
+                         "4096^3) from the native loop, for counting HIP API calls under rocprofv3 --hip-trace")
     ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: write the headline kernel's HBM-traffic record from two rocprofv3 passes")
     args = ap.parse_args()
@@ -227,6 +250,8 @@ def main() -> int:
         return 1
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
+    if args.api_loop:
+        return api_loop(args.api_loop, stream)
 
     log("generating the headline workload (MXFP8 4096^3)")
     p = si.workload("mxfp8_4096")
