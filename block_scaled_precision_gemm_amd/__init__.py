@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_nvfp4_f16",
-           "FORMATS", "OUT_DTYPES", "abi_version"]
+           "FORMATS", "OUT_DTYPES", "abi_version", "packed_strides", "Problem", "PROBLEM_V1_SIZE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsg.so")
@@ -40,7 +40,18 @@ class BsgError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("format", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("device", ctypes.c_int32)]
+                ("device", ctypes.c_int32), ("batch", ctypes.c_int32), ("stride_a", ctypes.c_int64),
+                ("stride_b", ctypes.c_int64), ("stride_sa", ctypes.c_int64), ("stride_sb", ctypes.c_int64),
+                ("stride_bias", ctypes.c_int64), ("stride_d", ctypes.c_int64)]
+
+
+PROBLEM_V1_SIZE = 48  # sizeof(bsg_problem) of ABI 1, still accepted by bsg_plan_create
+
+
+def packed_strides(fmt: str, M: int, N: int, K: int) -> dict:
+    """Byte strides of densely packed batched operands (bias shared by every problem)."""
+    elem, blk = (1.0, 32) if fmt == "mxfp8" else (0.5, 16)
+    return dict(a=int(M * K * elem), b=int(N * K * elem), sa=M * K // blk, sb=N * K // blk, bias=0, d=2 * M * N)
 
 
 class PlanInfo(ctypes.Structure):
@@ -119,16 +130,25 @@ def _stream(s) -> int | None:
 
 
 class Plan:
-    """A cached GEMM plan: D = epi(alpha * A x B^T (+ bias)) for one problem shape and variant."""
+    """A cached GEMM plan: D = epi(alpha * A x B^T (+ bias)) for one problem shape and variant.
+
+    batch > 1: that many problems of this shape per call; problem z uses each pointer advanced by
+    strides[key] * z bytes (keys a, b, sa, sb, bias, d; default: packed operands, shared bias).
+    """
 
     def __init__(self, fmt: str, M: int, N: int, K: int, out: str = "bf16", bias: bool = False,
-                 silu: bool = False, device: int = -1):
+                 silu: bool = False, device: int = -1, batch: int = 1, strides: dict | None = None):
         lib = load_library()
         self._lib = lib
         self._h = None
         self.fmt, self.M, self.N, self.K, self.out, self.bias, self.silu = fmt, M, N, K, out, bias, silu
+        self.batch = batch
+        st = packed_strides(fmt, M, N, K)
+        st.update(strides or {})
+        self.strides = st
         prob = Problem(ctypes.sizeof(Problem), FORMATS[fmt], OUT_DTYPES[out],
-                       (EPI_BIAS if bias else 0) | (EPI_SILU if silu else 0), M, N, K, device)
+                       (EPI_BIAS if bias else 0) | (EPI_SILU if silu else 0), M, N, K, device, batch,
+                       st["a"], st["b"], st["sa"], st["sb"], st["bias"], st["d"])
         h = _VP()
         _check(lib.bsg_plan_create(ctypes.byref(prob), ctypes.byref(h)))
         self._h = h

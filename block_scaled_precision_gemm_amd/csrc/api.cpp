@@ -9,6 +9,7 @@
 // bsg_run only patches pointers into a copy of the prebuilt argument block and launches.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
+#include <stddef.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -129,11 +130,30 @@ void device_free(int dev, void* p) {
   if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
 }
 
-bsg_status validate(const bsg_problem* p) {
-  if (p->struct_size != sizeof(bsg_problem)) {
-    set_error("bsg_problem.struct_size is %u, expected %zu", p->struct_size, sizeof(bsg_problem));
+static_assert(offsetof(bsg_problem, batch) == 44 && offsetof(bsg_problem, stride_a) == BSG_PROBLEM_V1_SIZE,
+              "the batch fields extend the ABI-1 layout (batch sits in its tail padding)");
+
+// Copy the caller's problem into `out`, reading only the bytes its struct_size covers: an ABI-1
+// problem (no batch fields) becomes a single problem.
+bsg_status normalize(const bsg_problem* in, bsg_problem* out) {
+  memset(out, 0, sizeof(*out));
+  if (in->struct_size == sizeof(bsg_problem)) {
+    *out = *in;
+  } else if (in->struct_size == BSG_PROBLEM_V1_SIZE) {
+    memcpy(out, in, offsetof(bsg_problem, batch));
+    out->struct_size = sizeof(bsg_problem);
+  } else {
+    set_error("bsg_problem.struct_size is %u, expected %zu (or %u for ABI 1)", in->struct_size, sizeof(bsg_problem),
+              BSG_PROBLEM_V1_SIZE);
     return BSG_ERR_ABI;
   }
+  if (out->batch == 0) out->batch = 1;
+  if (out->batch == 1) out->stride_a = out->stride_b = out->stride_sa = out->stride_sb = out->stride_bias =
+      out->stride_d = 0;
+  return BSG_OK;
+}
+
+bsg_status validate(const bsg_problem* p) {
   if (p->format != BSG_FMT_MXFP8 && p->format != BSG_FMT_NVFP4) {
     set_error("unknown format %d", p->format);
     return BSG_ERR_ABI;
@@ -170,6 +190,19 @@ bsg_status validate(const bsg_problem* p) {
     set_error("operand or output has >= 2^31 elements; not covered");
     return BSG_ERR_UNSUPPORTED;
   }
+  if (p->batch < 1 || p->batch > 65535) {
+    set_error("batch must be in [1, 65535] (got %d)", p->batch);
+    return p->batch < 1 ? BSG_ERR_SHAPE : BSG_ERR_UNSUPPORTED;
+  }
+  if (p->stride_a < 0 || p->stride_b < 0 || p->stride_sa < 0 || p->stride_sb < 0 || p->stride_bias < 0 ||
+      p->stride_d < 0) {
+    set_error("batch strides must be >= 0");
+    return BSG_ERR_SHAPE;
+  }
+  if (((p->stride_a | p->stride_b | p->stride_d) & 15) || ((p->stride_sa | p->stride_sb | p->stride_bias) & 3)) {
+    set_error("batch strides of A, B and D must be multiples of 16 bytes, of sA, sB and bias of 4");
+    return BSG_ERR_ALIGN;
+  }
   return BSG_OK;
 }
 
@@ -202,7 +235,11 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
     return BSG_ERR_NULL;
   }
   *out_plan = nullptr;
-  bsg_status st = validate(problem);
+  bsg_problem prob;
+  bsg_status st = normalize(problem, &prob);
+  if (st != BSG_OK) return st;
+  problem = &prob;
+  st = validate(problem);
   if (st != BSG_OK) return st;
   int dev = problem->device;
   if (dev < 0) {
@@ -218,7 +255,7 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   const bool bias = problem->flags & BSG_EPI_BIAS, silu = problem->flags & BSG_EPI_SILU;
   const bsg::Out out = problem->out_dtype == BSG_OUT_F16 ? bsg::Out::F16 : bsg::Out::BF16;
   const bsg::KernelVariant* table = problem->format == BSG_FMT_MXFP8
-                                        ? bsg::mxfp8_variants(problem->M, problem->N, problem->K)
+                                        ? bsg::mxfp8_variants(problem->M, problem->N, problem->K, problem->batch)
                                         : bsg::nvfp4_variants(problem->M, problem->N, problem->K);
   if (!table) {
     set_error("no kernel variant covers M=%lld N=%lld K=%lld", (long long)problem->M, (long long)problem->N,
@@ -251,9 +288,16 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   a.K = (int)problem->K;
   a.tiles_m = (int)((problem->M + v.tile_m - 1) / v.tile_m);
   a.tiles_n = (int)((problem->N + v.tile_n - 1) / v.tile_n);
-  a.splits = choose_splits(v, (int64_t)a.tiles_m * a.tiles_n, problem->K, g_dev_cus[dev]);
+  a.splits = choose_splits(v, (int64_t)a.tiles_m * a.tiles_n * problem->batch, problem->K, g_dev_cus[dev]);
+  a.stride_a = problem->stride_a;
+  a.stride_b = problem->stride_b;
+  a.stride_sa = problem->stride_sa;
+  a.stride_sb = problem->stride_sb;
+  a.stride_bias = problem->stride_bias;
+  a.stride_d = problem->stride_d;
   if (a.splits > 1) {
-    const size_t bytes = (size_t)a.splits * (size_t)problem->M * (size_t)problem->N * sizeof(float);
+    const size_t bytes =
+        (size_t)problem->batch * a.splits * (size_t)problem->M * (size_t)problem->N * sizeof(float);
     st = device_alloc(dev, bytes, &plan->workspace);
     if (st != BSG_OK) {
       delete plan;
@@ -262,8 +306,8 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
     plan->workspace_bytes = bytes;
     a.ws = (float*)plan->workspace;
   }
-  plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n * a.splits), 1, 1)
-                             : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, 1);
+  plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n * a.splits), 1, (unsigned)problem->batch)
+                             : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, (unsigned)problem->batch);
   plan->block = dim3((unsigned)v.block_threads, 1, 1);
   *out_plan = plan;
   return BSG_OK;

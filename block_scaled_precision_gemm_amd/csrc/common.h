@@ -29,8 +29,23 @@ struct GemmArgs {
   int M, N, K;
   int tiles_m, tiles_n;   // output tile grid
   int splits;             // split-K factor (1: none)
-  float* ws;              // split-K partials [splits][M][N] fp32 (plan-owned), or null
+  float* ws;              // split-K partials [batch][splits][M][N] fp32 (plan-owned), or null
+  // Batched problems: grid.z = batch count; batch z uses each pointer advanced by z * its stride
+  // (bytes; a stride of 0 shares one matrix / bias vector among all batches).
+  int64_t stride_a, stride_b, stride_sa, stride_sb, stride_bias, stride_d;
 };
+
+// Move this workgroup's operand, output and workspace pointers to its batch (blockIdx.z).
+__device__ __forceinline__ void select_batch(GemmArgs& p) {
+  const int64_t z = blockIdx.z;
+  p.A += z * p.stride_a;
+  p.B += z * p.stride_b;
+  p.sA += z * p.stride_sa;
+  p.sB += z * p.stride_sb;
+  p.bias = (const float*)((const uint8_t*)p.bias + z * p.stride_bias);
+  p.D = (uint8_t*)p.D + z * p.stride_d;
+  if (p.ws) p.ws += z * (int64_t)p.splits * p.M * p.N;
+}
 
 // A launcher: enqueues one kernel on `stream` with a precomputed launch shape.  Kernels use static
 // LDS only; no dynamic LDS is requested at launch.
@@ -48,8 +63,9 @@ struct KernelVariant {
 
 // Variant tables, one per format: index = out dtype (0 bf16, 1 f16) * 4 + bias * 2 + silu.
 // Each kernel family returns its table for the M bucket it serves.
-const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K);
-const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N);
+// `batch`: problems per launch (the grid holds tiles x batch workgroups).
+const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K, int64_t batch);
+const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N, int64_t batch);
 const KernelVariant* mxfp8_pp_variants();
 const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K);
 

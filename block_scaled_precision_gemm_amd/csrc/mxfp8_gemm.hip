@@ -39,6 +39,7 @@ __device__ __forceinline__ v8i join(v4i lo, v4i hi) {
 // ---------------------------------------------------------------------------------------------
 template <Out O, bool BIAS, bool SILU>
 __global__ __launch_bounds__(256) void mxfp8_direct_kernel(GemmArgs p) {
+  select_batch(p);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 31, h = lane >> 5;
@@ -100,10 +101,10 @@ const KernelVariant kDirect[8] = {
 // Kernel choice by shape: the 4-wave pipelined kernel for K % 512 == 0 once 256 x 256 tiles give at
 // least one workgroup per CU; the two-stage tiled kernels for other K % 128 == 0; the direct kernel
 // for the remaining K % 32 == 0.
-const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K) {
-  const int64_t large_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  const int64_t large_tiles = ((M + 255) / 256) * ((N + 255) / 256) * batch;
   if (K % 512 == 0 && large_tiles >= 256) return mxfp8_pp_variants();
-  return K % 128 == 0 ? mxfp8_tiled_variants(M, N) : kDirect;
+  return K % 128 == 0 ? mxfp8_tiled_variants(M, N, batch) : kDirect;
 }
 
 }  // namespace bsg

@@ -101,6 +101,7 @@ __device__ __forceinline__ void phase_end() {
 
 template <Out O, bool BIAS, bool SILU>
 __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
+  select_batch(p);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
   uint8_t* const scale_lds = lds + NS * (A_TILE + B_TILE);  // two buffers: [A rows][16], [B rows][16]
 

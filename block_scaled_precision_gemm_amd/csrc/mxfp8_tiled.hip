@@ -95,6 +95,7 @@ struct CopyPlan {
 
 template <class C, Out O, bool BIAS, bool SILU>
 __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
+  select_batch(p);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
   constexpr int TM = C::TM, TN = C::TN;
 
@@ -258,8 +259,8 @@ const KernelVariant kSmall[8] = BSG_MX_TABLE("mxfp8_tiled_128x128x128_w4", Small
 }  // namespace mxt
 
 // Large tiles once they give at least one workgroup per CU (256 CUs); smaller tiles otherwise.
-const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N) {
-  const int64_t large_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N, int64_t batch) {
+  const int64_t large_tiles = ((M + 255) / 256) * ((N + 255) / 256) * batch;
   return large_tiles >= 256 ? mxt::kLarge : mxt::kSmall;
 }
 

@@ -102,6 +102,7 @@ __device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
 
 template <bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT>
 __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
+  select_batch(p);
   constexpr int BM = SHARED_A ? BS : BP, BN = SHARED_A ? BP : BS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   uint8_t* const raw = lds;
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 // order.  One thread per 4 consecutive columns (N % 16 == 0).
 template <Out O, bool BIAS, bool SILU>
 __global__ __launch_bounds__(256) void nvfp4_splitk_finish_kernel(GemmArgs p) {
+  select_batch(p);
   const int nq = p.N >> 2;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)p.M * nq) return;
@@ -367,7 +369,7 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
   if (e != hipSuccess) return e;
   const int64_t threads = (int64_t)args.M * (args.N >> 2);
   return hipLaunchKernel((const void*)&nvfp4_splitk_finish_kernel<O, BIAS, SILU>,
-                         dim3((unsigned)((threads + 255) / 256)), dim3(256), kargs, 0, stream);
+                         dim3((unsigned)((threads + 255) / 256), 1, grid.z), dim3(256), kargs, 0, stream);
 }
 
 #define BSG_NVR(SA, NAME, O, B, S) \

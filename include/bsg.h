@@ -34,7 +34,8 @@
  *                             allocates the plan's device workspace if the
  *                             variant splits K (bsg_plan_info.workspace_bytes).
  *   bsg_run(plan, ...)        per call: O(1) pointer checks and one or two
- *                             kernel launches on the caller's stream.  No
+ *                             kernel launches on the caller's stream (a
+ *                             batched plan runs all its problems in them).  No
  *                             allocation, no synchronisation, no device query,
  *                             so it may be captured into a HIP graph.
  *   bsg_plan_destroy(plan)    frees the plan and its workspace.
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define BSG_ABI_VERSION 1
+#define BSG_ABI_VERSION 2
 
 typedef enum bsg_status {
   BSG_OK = 0,
@@ -91,13 +92,24 @@ enum {
 };
 
 typedef struct bsg_problem {
-  uint32_t struct_size; /* = sizeof(bsg_problem), else BSG_ERR_ABI */
+  uint32_t struct_size; /* = sizeof(bsg_problem), or BSG_PROBLEM_V1_SIZE (then batch = 1); else BSG_ERR_ABI */
   int32_t format;       /* bsg_format */
   int32_t out_dtype;    /* bsg_out_dtype */
   uint32_t flags;       /* BSG_EPI_* */
   int64_t M, N, K;      /* M >= 1; N >= 16, N % 16 == 0; K >= 32, K % 32 == 0 (MXFP8) or K % 16 == 0 (NVFP4) */
   int32_t device;       /* HIP device ordinal; -1 = the current device at create time */
+  /* Batched GEMM (ABI 2): `batch` independent problems of the same shape in one launch.  Problem z
+   * (0 <= z < batch) reads A + z*stride_a, B + z*stride_b, sA + z*stride_sa, sB + z*stride_sb and
+   * bias + z*stride_bias (bytes), and writes D + z*stride_d.  A stride of 0 makes every problem use
+   * the same operand (e.g. shared weights B, or one bias vector); strides must be >= 0, multiples
+   * of 16 for A, B and D and of 4 for sA, sB and bias, and distinct problems' D must not overlap
+   * (not checked).  batch 0 is read as 1; strides are ignored when batch is 1. */
+  int32_t batch;
+  int64_t stride_a, stride_b, stride_sa, stride_sb, stride_bias, stride_d;
 } bsg_problem;
+
+/* sizeof(bsg_problem) of ABI 1 (no batch fields): still accepted, as a single problem. */
+#define BSG_PROBLEM_V1_SIZE 48u
 
 typedef struct bsg_plan_s* bsg_plan; /* opaque, library-owned */
 
@@ -107,7 +119,8 @@ typedef struct bsg_plan_info {
   int32_t tile_m, tile_n, tile_k;
   uint32_t grid_x, grid_y, grid_z, block_x;
   uint32_t lds_bytes;
-  uint64_t workspace_bytes; /* device workspace the plan owns (0: none); grid_x includes the split-K factor */
+  uint64_t workspace_bytes; /* device workspace the plan owns (0: none); grid_x includes the split-K factor,
+                               grid_z is the batch count */
 } bsg_plan_info;
 
 /* Validate `problem`, choose the kernel variant for (format, out dtype, epilogue, M bucket) and

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = bsg.load_library()
-    assert lib.bsg_abi_version() == 1
+    assert lib.bsg_abi_version() == 2
     for code, name in bsg.STATUS.items():
         assert lib.bsg_status_string(code).decode() == name
 
@@ -52,6 +52,51 @@ def test_plan_create_validation(field, value, status):
     st, h = _create(**{field: value})
     assert st == status, bsg.load_library().bsg_last_error()
     assert not h.value
+
+
+@pytest.mark.parametrize("fields,status", [
+    (dict(batch=-1), 2), (dict(batch=65536), 3),
+    (dict(batch=2, stride_a=-16), 2), (dict(batch=2, stride_d=-32), 2),
+    (dict(batch=2, stride_a=8), 4), (dict(batch=2, stride_b=24), 4), (dict(batch=2, stride_d=100), 4),
+    (dict(batch=2, stride_sa=2), 4), (dict(batch=2, stride_bias=6), 4),
+])
+def test_batched_plan_validation(fields, status):
+    st, h = _create(**fields)
+    assert st == status, bsg.load_library().bsg_last_error()
+    assert not h.value
+
+
+def test_abi1_problem_size_is_accepted():
+    """An ABI-1 caller (48-byte bsg_problem, no batch fields) still passes validation: without a GPU
+    it reaches the device check; any other size is an ABI error."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, _ = _create(struct_size=bsg.PROBLEM_V1_SIZE, batch=7, stride_a=3)  # bytes past 48 are not read
+    assert st == 5, bsg.load_library().bsg_last_error()
+    st, _ = _create(struct_size=bsg.PROBLEM_V1_SIZE + 8)
+    assert st == 8
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """The ctypes mirrors of bsg_problem / bsg_plan_info have the C layout (compiled with gcc)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "bsg.h"\n'
+        "int main(void) { printf(\"%zu %zu %zu %zu %zu %zu %u\\n\", sizeof(bsg_problem), offsetof(bsg_problem, device),"
+        " offsetof(bsg_problem, batch), offsetof(bsg_problem, stride_a), offsetof(bsg_problem, stride_d),"
+        " sizeof(bsg_plan_info), BSG_PROBLEM_V1_SIZE); return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    P = bsg.Problem
+    want = [ctypes.sizeof(P), P.device.offset, P.batch.offset, P.stride_a.offset, P.stride_d.offset,
+            ctypes.sizeof(bsg.PlanInfo), bsg.PROBLEM_V1_SIZE]
+    assert got == want
 
 
 def test_nvfp4_k_rules():

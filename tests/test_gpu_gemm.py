@@ -5,6 +5,7 @@ import torch
 
 import block_scaled_precision_gemm_amd as bsg
 import seeded_inputs as si
+from gpu_util import exact_regime_problem as _exact_regime_problem
 from gpu_util import make_plan, run, to_device
 from oracle import compare, reference
 
@@ -25,26 +26,6 @@ def _check(p, rows=None, rel=1e-2):
           f"max_err/S={rep['max_err_over_S']:.3g} by_floor={rep['n_passed_by_floor']}/{rep['n']}", flush=True)
     assert rep["ok"], rep
     return rep
-
-
-def _exact_regime_problem(fmt, M, N, K, seed, out):
-    """Products confined to a narrow exponent range with per-row / per-column constant scales: the
-    MFMA's internal alignment then drops no bit and every fp32 partial sum is exact, so D must equal
-    the oracle bit for bit."""
-    g = np.random.default_rng(seed)
-    if fmt == "mxfp8":  # E4M3 elements +-[1, 1.875] (exponent field 7), E8M0 scales constant along K
-        A = ((g.integers(0, 2, (M, K)) << 7) | (7 << 3) | g.integers(0, 8, (M, K))).astype(np.uint8)
-        B = ((g.integers(0, 2, (N, K)) << 7) | (7 << 3) | g.integers(0, 8, (N, K))).astype(np.uint8)
-        sA = np.repeat(g.integers(118, 136, (M, 1)), K // 32, axis=1).astype(np.uint8)
-        sB = np.repeat(g.integers(118, 136, (N, 1)), K // 32, axis=1).astype(np.uint8)
-    else:  # E2M1 elements +-{1, 1.5}, E4M3 scales constant along K
-        qa = (g.integers(0, 2, (M, K)) << 3 | g.integers(2, 4, (M, K))).astype(np.uint8)
-        qb = (g.integers(0, 2, (N, K)) << 3 | g.integers(2, 4, (N, K))).astype(np.uint8)
-        A, B = si.pack_e2m1(qa), si.pack_e2m1(qb)
-        sA = np.repeat(g.integers(0x20, 0x50, (M, 1)), K // 16, axis=1).astype(np.uint8)
-        sB = np.repeat(g.integers(0x20, 0x50, (N, 1)), K // 16, axis=1).astype(np.uint8)
-    return dict(fmt=fmt, M=M, N=N, K=K, A=A, B=B, sA=sA, sB=sB, alpha=np.float32(0.5), bias=None, silu=False,
-                out=out)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
