@@ -18,12 +18,16 @@
 // * Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives each XCD a
 //   contiguous range of tiles, walked in groups of 8 tile-rows, so that concurrently resident
 //   workgroups of one XCD share A and B panels in its L2.
+// * Split-K (SPLIT, small tile grids): workgroup id = split * tiles + tile; split s covers a
+//   contiguous range of K tiles and writes its fp32 sums to the plan's workspace ws[s][m][n], which
+//   splitk.h's finish kernel adds in split order and finishes (alpha, bias, SiLU, rounding).
 //
 // Operand register layout of the scaled MFMA (measured on the device): lane l (r = l % 32,
 // h = l / 32) holds K bytes [16h, 16h+16) and [32+16h, 32+16h+16) of its row, and its scale
 // byte is the E8M0 code of 32-block h.  Accumulator element e: row 8*(e/4) + 4*h + e%4, column r.
 #include "common.h"
 #include "epilogue.h"
+#include "splitk.h"
 
 namespace bsg {
 // Named (not anonymous) namespace: kernel templates instantiated on these configuration types need
@@ -35,9 +39,9 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int MAX_SPLITS_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MAX_SPLITS = MAX_SPLITS_;
   static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
   static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
   static constexpr int A_TILE = BM * BK, B_TILE = BN * BK, STAGE = A_TILE + B_TILE;
@@ -93,7 +97,7 @@ struct CopyPlan {
   }
 };
 
-template <class C, Out O, bool BIAS, bool SILU>
+template <class C, Out O, bool BIAS, bool SILU, bool SPLIT>
 __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
   select_batch(p);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
@@ -103,9 +107,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31, h = lane >> 5;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int2 t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n);
+  const int T = p.tiles_m * p.tiles_n;
+  int bid = blockIdx.x, kt_begin = 0, kt_end = p.K / BK;
+  if constexpr (SPLIT) {  // split-major ids; split s gets K tiles [s KT / S, (s + 1) KT / S)
+    const int s = bid / T;
+    bid -= s * T;
+    kt_begin = (int)((int64_t)s * kt_end / p.splits);
+    kt_end = (int)((int64_t)(s + 1) * kt_end / p.splits);
+  }
+  const int2 t = tile_of(bid, p.tiles_m, p.tiles_n);
   const int m0 = t.x * C::BM, n0 = t.y * C::BN;
-  const int K = p.K, KB = K >> 5, KT = K / BK;
+  const int K = p.K, KB = K >> 5;
   const int m_valid = min(C::BM, p.M - m0), n_valid = min(C::BN, p.N - n0);
 
   // operand buffers start at the tile's first row and end at the last valid row
@@ -145,24 +157,28 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (v16f){};
 
-  // prologue: tile 0 -> stage 0, scales of tile 0 -> registers
-  cpA.issue(rsA, 0, lds);
-  cpB.issue(rsB, 0, lds + C::A_TILE);
+  // prologue: first K tile -> stage 0, its scales -> registers
+  cpA.issue(rsA, (uint32_t)kt_begin * BK, lds);
+  cpB.issue(rsB, (uint32_t)kt_begin * BK, lds + C::A_TILE);
   uint32_t sa_next[TM], sb_next[TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][0];
+  for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][kt_begin];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][0];
+  for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][kt_begin];
 
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     uint32_t sa_cur[TM], sb_cur[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) sa_cur[i] = sa_next[i];
 #pragma unroll
     for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
-    __syncthreads();  // tile kt is in LDS stage kt&1; everyone is done reading stage (kt+1)&1
-    if (kt + 1 < KT) {
-      uint8_t* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+    // LDS-DMA copies count in vmcnt only; the barrier does not wait for them, and the compiler waits
+    // only before this wave's own LDS reads, so each wave drains its copies of tile kt here: after
+    // the barrier the whole tile is in its stage and everyone is done reading the other one.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < kt_end) {
+      uint8_t* nxt = lds + ((kt + 1 - kt_begin) & 1) * C::STAGE;
       const uint32_t k1 = (uint32_t)(kt + 1) * BK;
       cpA.issue(rsA, k1, nxt);
       cpB.issue(rsB, k1, nxt + C::A_TILE);
@@ -171,7 +187,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 #pragma unroll
       for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][kt + 1];
     }
-    const uint8_t* a_lds = lds + (kt & 1) * C::STAGE;
+    const uint8_t* a_lds = lds + ((kt - kt_begin) & 1) * C::STAGE;
     const uint8_t* b_lds = a_lds + C::A_TILE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -198,6 +214,24 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
     }
   }
 
+  if constexpr (SPLIT) {  // fp32 partial sums of this K range, unscaled
+    float* ws = p.ws + (size_t)(blockIdx.x / T) * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * TN * 32 + 32 * j + r;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * TM * 32 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (m < p.M) ws[(size_t)m * p.N + n] = acc[i][j][e];
+        }
+      }
+    }
+    return;
+  }
+
   // epilogue
   const float alpha = load_alpha(p);
   uint16_t* D = (uint16_t*)p.D;
@@ -220,11 +254,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 template <class C, Out O, bool BIAS, bool SILU>
 hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
-  return hipLaunchKernel((const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU>, grid, block, kargs, 0, stream);
+  if (args.splits <= 1)
+    return hipLaunchKernel((const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false>, grid, block, kargs, 0, stream);
+  const hipError_t e =
+      hipLaunchKernel((const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true>, grid, block, kargs, 0, stream);
+  if (e != hipSuccess) return e;
+  return launch_splitk_finish<O, BIAS, SILU, 0>(args, grid.z, stream);
 }
 
 #define BSG_MX_TILED(NAME, C, O, B, S) \
-  { NAME, &launch_tiled<C, O, B, S>, C::BM, C::BN, BK, C::THREADS, 2 * C::STAGE, true }
+  { NAME, &launch_tiled<C, O, B, S>, C::BM, C::BN, BK, C::THREADS, 2 * C::STAGE, true, C::MAX_SPLITS }
 #define BSG_MX_TABLE(NAME, C)                                                                    \
   {                                                                                              \
     BSG_MX_TILED(NAME, C, Out::BF16, false, false), BSG_MX_TILED(NAME, C, Out::BF16, false, true), \
@@ -233,22 +272,24 @@ hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t
     BSG_MX_TILED(NAME, C, Out::F16, true, false), BSG_MX_TILED(NAME, C, Out::F16, true, true)      \
   }
 
-using Large = Cfg<256, 256, 2, 4>;  // 8 waves of 128 x 64
-using Small = Cfg<128, 128, 2, 2>;  // 4 waves of 64 x 64, for problems with few large tiles
+using Large = Cfg<256, 256, 2, 4, 1>;   // 8 waves of 128 x 64 (enough tiles to fill the chip: no split)
+using Small = Cfg<128, 128, 2, 2, 16>;  // 4 waves of 64 x 64, for problems with few large tiles
 
 // Explicit instantiations: taking a kernel template's address only inside another template does not
 // make the compiler emit its host-side launch stub when the template argument is a class type.
-#define BSG_MX_INST(C)                                                            \
-  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, false>(GemmArgs); \
-  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, true>(GemmArgs);  \
-  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, false>(GemmArgs);  \
-  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, true>(GemmArgs);   \
-  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, false>(GemmArgs);  \
-  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, true>(GemmArgs);   \
-  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, false>(GemmArgs);   \
-  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, true>(GemmArgs);
-BSG_MX_INST(Large)
-BSG_MX_INST(Small)
+#define BSG_MX_INST(C, SP)                                                            \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, false, SP>(GemmArgs); \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, true, SP>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, false, SP>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, true, SP>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, false, SP>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, true, SP>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, false, SP>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, true, SP>(GemmArgs);
+BSG_MX_INST(Large, false)
+BSG_MX_INST(Large, true)
+BSG_MX_INST(Small, false)
+BSG_MX_INST(Small, true)
 #undef BSG_MX_INST
 
 const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);

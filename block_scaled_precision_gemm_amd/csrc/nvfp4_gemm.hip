@@ -47,6 +47,7 @@
 #include "codec.h"
 #include "common.h"
 #include "epilogue.h"
+#include "splitk.h"
 
 namespace bsg {
 namespace nvr {
@@ -338,27 +339,6 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   }
 }
 
-// Split-K finish: D[m][n] = epi(alpha * 2^16 * sum_s ws[s][m][n] (+ bias[n])), summed in split
-// order.  One thread per 4 consecutive columns (N % 16 == 0).
-template <Out O, bool BIAS, bool SILU>
-__global__ __launch_bounds__(256) void nvfp4_splitk_finish_kernel(GemmArgs p) {
-  select_batch(p);
-  const int nq = p.N >> 2;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)p.M * nq) return;
-  const int m = (int)(idx / nq), n = (int)(idx - (int64_t)m * nq) * 4;
-  const size_t plane = (size_t)p.M * p.N;
-  const float* src = p.ws + (size_t)m * p.N + n;
-  v4f s = *(const v4f*)src;
-  for (int k = 1; k < p.splits; ++k) s += *(const v4f*)(src + k * plane);
-  const float alpha = load_alpha(p) * kRescale;
-  v4f b = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};  // bias: 4-byte aligned
-  uint32_t* D = (uint32_t*)((uint16_t*)p.D + (size_t)m * p.N + n);
-  D[0] = pack2_out<O>(epi_value<SILU>(s[0], alpha, b[0]), epi_value<SILU>(s[1], alpha, b[1]));
-  D[1] = pack2_out<O>(epi_value<SILU>(s[2], alpha, b[2]), epi_value<SILU>(s[3], alpha, b[3]));
-}
-
 template <bool SHARED_A, Out O, bool BIAS, bool SILU>
 hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
@@ -367,9 +347,7 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
   hipError_t e =
       hipLaunchKernel((const void*)&nvfp4_kernel<SHARED_A, O, BIAS, SILU, true>, grid, block, kargs, 0, stream);
   if (e != hipSuccess) return e;
-  const int64_t threads = (int64_t)args.M * (args.N >> 2);
-  return hipLaunchKernel((const void*)&nvfp4_splitk_finish_kernel<O, BIAS, SILU>,
-                         dim3((unsigned)((threads + 255) / 256), 1, grid.z), dim3(256), kargs, 0, stream);
+  return launch_splitk_finish<O, BIAS, SILU, 16>(args, grid.z, stream);  // accumulators carry 2^-16
 }
 
 #define BSG_NVR(SA, NAME, O, B, S) \

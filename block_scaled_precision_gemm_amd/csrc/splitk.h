@@ -1,0 +1,44 @@
+// Split-K finish kernel shared by the kernels that split K over workgroups.
+//
+// A split plan's GEMM kernel writes fp32 partial sums ws[z][s][m][n] (batch z, split s) of its K range
+// into the plan's workspace; this kernel adds the S partials of each element in split order (a fixed
+// order, so results are deterministic), applies the epilogue of epilogue.h (alpha, bias, SiLU, one
+// rounding) and writes D.  RESCALE multiplies alpha for kernels whose accumulators carry a known
+// power-of-two factor (the NVFP4 fp16 route: 2^-16).  One thread per 4 consecutive columns
+// (N % 16 == 0); grid.z = batch.
+#pragma once
+
+#include "common.h"
+#include "epilogue.h"
+
+namespace bsg {
+
+template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
+  select_batch(p);
+  const int nq = p.N >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.M * nq) return;
+  const int m = (int)(idx / nq), n = (int)(idx - (int64_t)m * nq) * 4;
+  const size_t plane = (size_t)p.M * p.N;
+  const float* src = p.ws + (size_t)m * p.N + n;
+  v4f s = *(const v4f*)src;
+  for (int k = 1; k < p.splits; ++k) s += *(const v4f*)(src + k * plane);
+  const float alpha = load_alpha(p) * (float)(1u << RESCALE_LOG2);
+  v4f b = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};  // bias: 4-byte aligned
+  uint32_t* D = (uint32_t*)((uint16_t*)p.D + (size_t)m * p.N + n);
+  D[0] = pack2_out<O>(epi_value<SILU>(s[0], alpha, b[0]), epi_value<SILU>(s[1], alpha, b[1]));
+  D[1] = pack2_out<O>(epi_value<SILU>(s[2], alpha, b[2]), epi_value<SILU>(s[3], alpha, b[3]));
+}
+
+// Enqueue the finish kernel of a split plan (grid.z of the GEMM launch = batch).
+template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2>
+hipError_t launch_splitk_finish(const GemmArgs& args, unsigned batch, hipStream_t stream) {
+  void* kargs[] = {(void*)&args};
+  const int64_t threads = (int64_t)args.M * (args.N >> 2);
+  return hipLaunchKernel((const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2>,
+                         dim3((unsigned)((threads + 255) / 256), 1, batch), dim3(256), kargs, 0, stream);
+}
+
+}  // namespace bsg

@@ -58,13 +58,14 @@ def _share(problems, keys):
     ("mxfp8", (96, 64, 256), 3), ("nvfp4", (96, 64, 256), 3),
     ("mxfp8", (1024, 1024, 512), 16),   # 16 tiles x 16 problems: the large-shape kernel
     ("nvfp4", (128, 1024, 4096), 2),    # split-K with one workspace slice per problem
+    ("mxfp8", (128, 1024, 4096), 2),
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_batched_exact_regime_bit_exact(fmt, shape, L):
     M, N, K = shape
     problems = [exact_regime_problem(fmt, M, N, K, seed=1000 * z + K, out="bf16") for z in range(L)]
     outs, info = _run_batched(problems, {})
     assert info["grid"][2] == L
-    if fmt == "nvfp4" and K == 4096:  # split K: the workspace holds L x splits x M x N fp32 partials
+    if K == 4096:  # split K: the workspace holds L x splits x M x N fp32 partials
         splits = info["grid"][0] // (N // info["tile"][1])
         assert splits > 1 and info["workspace_bytes"] == L * splits * M * N * 4
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 8)), [M - 1]]))

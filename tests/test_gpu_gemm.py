@@ -275,6 +275,54 @@ def _graph_replay_matches_eager(plan, problems):
         assert np.array_equal(d["D"].cpu().numpy().view(np.uint16), want)
 
 
+# MXFP8 problems with too few 256 x 256 tiles to fill the chip run 128 x 128 tiles and, when those are
+# still fewer than the CUs, split K the same way; shapes cover split and unsplit plans, ragged M / N,
+# a split count that does not divide the K tiles, and K not a multiple of 512.
+MXFP8_SPLIT_SHAPES = [(100, 80, 1024), (1, 16, 4096), (129, 4000, 2048), (256, 1024, 1152), (640, 4096, 384),
+                      (512, 1024, 4096), (1024, 1024, 1024), (33, 2000, 1408)]
+
+
+@pytest.mark.parametrize("shape", MXFP8_SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("epi", ["plain", "bias_silu_f16"])
+def test_mxfp8_split_k(shape, epi):
+    M, N, K = shape
+    plain = epi == "plain"
+    p = si.problem("mxfp8", M, N, K, seed=700 + M + N + K, bias=not plain, silu=not plain,
+                   out="bf16" if plain else "f16", alpha=0.75)
+    plan = make_plan(p)
+    info = plan.info()
+    tiles = -(-M // info["tile"][0]) * -(-N // info["tile"][1])
+    splits = info["grid"][0] // tiles
+    assert info["grid"][0] == tiles * splits
+    assert info["workspace_bytes"] == (0 if splits == 1 else splits * M * N * 4)
+    print(f"[plan] {shape} {info['variant']} splits={splits}", flush=True)
+    D = run(p, plan=plan)
+    rep = compare(D, reference(p), p["alpha"], p["silu"], p["out"])
+    assert rep["ok"], rep
+
+
+def test_mxfp8_split_k_plans():
+    # 64 tiles of 128 x 128: four K splits fill the 256 CUs
+    info = bsg.Plan("mxfp8", 128, 8192, 8192, out="bf16").info()
+    assert info["variant"].startswith("mxfp8_tiled_128x128")
+    assert info["grid"][0] == 64 * 4 and info["workspace_bytes"] == 4 * 128 * 8192 * 4
+    # at most one split per 4 K tiles of 128
+    info = bsg.Plan("mxfp8", 256, 256, 256, out="bf16").info()
+    assert info["grid"][0] == 4 and info["workspace_bytes"] == 0
+
+
+def test_mxfp8_split_k_exact_regime_bit_exact_and_graph():
+    """In the exact regime every partial sum is exact in fp32, so any split gives the oracle's bits."""
+    p = _exact_regime_problem("mxfp8", 128, 2048, 4096, seed=77, out="bf16")
+    plan = make_plan(p)
+    info = plan.info()
+    assert info["grid"][0] // 16 > 1, info
+    D = run(p, plan=plan)
+    assert np.array_equal(D, reference(p)["bits"])
+    q = si.problem("mxfp8", 128, 2048, 4096, seed=78, out="bf16", alpha=0.5)
+    _graph_replay_matches_eager(plan, [p, q])
+
+
 def test_nvfp4_split_k_deterministic_alpha_ptr_and_graph():
     p = si.problem("nvfp4", 256, 1024, 4096, seed=1234, bias=True, silu=True, out="bf16", alpha=0.3)
     plan = make_plan(p)
