@@ -13,7 +13,13 @@ sets x 100 calls) as host wall time per call vs GPU time per call, direct and fr
 The CPU baseline is the fp64 oracle (test infrastructure) timed on the host cores on a bounded sample
 of rows of the headline workload.
 
+Scales are row-major by default (the ABI default).  --scale-layout ktile runs every workload on the
+library's K-tile-major scale layout instead (BSG_SCALES_KTILE; scales converted by bsg_pack_scales
+before timing, as the MXFP8 page's test swizzles its scales before the GEMM); the default run also
+reports the headline and the NVFP4 128x8192x8192 workload on that layout in "extra".
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-main] [--calibration-copy]
+                       [--scale-layout linear|ktile]
        python bench.py --counters-from FETCH_CSV WRITE_CSV   (records HBM traffic from rocprofv3 passes)
        python bench.py --api-loop N   (N direct calls per workload only, for rocprofv3 --hip-trace)
 """
@@ -94,21 +100,30 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def device_inputs(p: dict):
+def device_inputs(p: dict, scale_layout: str = "linear"):
     import numpy as np
     import torch
+    import block_scaled_precision_gemm_amd as bsg
     d = {k: torch.from_numpy(np.ascontiguousarray(p[k])).cuda() for k in ("A", "B", "sA", "sB")}
+    if scale_layout == "ktile":  # one-time layout conversion, outside any timed region
+        for key, rows in (("sA", p["M"]), ("sB", p["N"])):
+            kb = p[key].shape[1]
+            packed = torch.empty(bsg.scales_ktile_bytes(rows, kb), dtype=torch.uint8, device="cuda")
+            bsg.pack_scales(d[key], packed, rows, kb)
+            d[key] = packed
+        torch.cuda.synchronize()
     d["bias"] = None if p["bias"] is None else torch.from_numpy(np.ascontiguousarray(p["bias"])).cuda()
     d["D"] = torch.empty((p["M"], p["N"]), dtype=torch.int16, device="cuda")
     return d
 
 
-def time_gemm(p: dict, steps: int, warmup: int, stream) -> dict:
+def time_gemm(p: dict, steps: int, warmup: int, stream, scale_layout: str = "linear") -> dict:
     """Warm up, then time `steps` back-to-back calls on `stream` (host wall and HIP events)."""
     import torch
     import block_scaled_precision_gemm_amd as bsg
-    plan = bsg.Plan(p["fmt"], p["M"], p["N"], p["K"], out=p["out"], bias=p["bias"] is not None, silu=p["silu"])
-    d = device_inputs(p)
+    plan = bsg.Plan(p["fmt"], p["M"], p["N"], p["K"], out=p["out"], bias=p["bias"] is not None, silu=p["silu"],
+                    scale_layout=scale_layout)
+    d = device_inputs(p, scale_layout)
     args = (d["A"], d["B"], d["sA"], d["sB"], d["D"])
     kw = dict(alpha=float(p["alpha"]), bias=d["bias"], stream=stream)
     for _ in range(warmup):
@@ -131,17 +146,17 @@ def time_gemm(p: dict, steps: int, warmup: int, stream) -> dict:
                 tflops_wall=flops / (wall_ms * 1e-3) / 1e12, tflops_gpu=flops / (gpu_ms * 1e-3) / 1e12, flops=flops)
 
 
-def loop_bench(stream, n_sets: int = 10, calls: int = 100) -> dict:
+def loop_bench(stream, n_sets: int = 10, calls: int = 100, scale_layout: str = "linear") -> dict:
     """Looped small-M NVFP4 GEMM: n_sets fresh seeded input sets x `calls` back-to-back calls."""
     import torch
     import block_scaled_precision_gemm_amd as bsg
     import seeded_inputs as si
     sets_host = [si.workload("nvfp4_256x4096x4096_loop", set_id=s) for s in range(n_sets)]
     p0 = sets_host[0]
-    plan = bsg.Plan("nvfp4", p0["M"], p0["N"], p0["K"], out="bf16")
+    plan = bsg.Plan("nvfp4", p0["M"], p0["N"], p0["K"], out="bf16", scale_layout=scale_layout)
     sets = []
     for p in sets_host:
-        d = device_inputs(p)
+        d = device_inputs(p, scale_layout)
         d["alpha"] = float(p["alpha"])
         sets.append(d)
     # warm-up (first-launch costs, caches)
@@ -231,6 +246,8 @@ def main() -> int:
     ap.add_argument("--api-loop", type=int, metavar="N",
                     help="only run N direct bsg_run calls per workload (NVFP4 256x4096x4096 split-K, MXFP8 "
                          "4096^3) from the native loop, for counting HIP API calls under rocprofv3 --hip-trace")
+    ap.add_argument("--scale-layout", choices=("linear", "ktile"), default="linear",
+                    help="scale layout of every workload (default: row-major, the ABI default)")
     ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: write the headline kernel's HBM-traffic record from two rocprofv3 passes")
     args = ap.parse_args()
@@ -255,7 +272,8 @@ def main() -> int:
 
     log("generating the headline workload (MXFP8 4096^3)")
     p = si.workload("mxfp8_4096")
-    main_r = time_gemm(p, args.steps, args.warmup, stream)
+    lay = args.scale_layout
+    main_r = time_gemm(p, args.steps, args.warmup, stream, lay)
     log(f"main: {main_r}")
     if args.calibration_copy:
         n = 1 << 28  # 256 MiB read + 256 MiB written per copy
@@ -273,7 +291,7 @@ def main() -> int:
                                   ("mxfp8_256", 500, 500)):
             log(f"workload {name}")
             q = si.workload(name)
-            r = time_gemm(q, steps, warm, stream)
+            r = time_gemm(q, steps, warm, stream, lay)
             peak = PEAK_TFLOPS["mxfp8"] if q["fmt"] == "mxfp8" else PEAK_TFLOPS["nvfp4_fp4"]
             r["frac_of_mx_peak"] = r["tflops_gpu"] / peak
             if q["fmt"] == "nvfp4":
@@ -282,8 +300,15 @@ def main() -> int:
             log(f"{name}: {extra[name]}")
         log("looped NVFP4 256x4096x4096, 10 sets x 100 calls")
         extra["nvfp4_256x4096x4096_loop"] = {k: (round(v, 3) if isinstance(v, float) else v)
-                                             for k, v in loop_bench(stream).items()}
+                                             for k, v in loop_bench(stream, scale_layout=lay).items()}
         log(f"loop: {extra['nvfp4_256x4096x4096_loop']}")
+        if lay == "linear":
+            for name, steps, warm in (("mxfp8_4096", args.steps, 100), ("nvfp4_128x8192x8192_silu", 200, 100)):
+                q = p if name == "mxfp8_4096" else si.workload(name)
+                r = time_gemm(q, steps, warm, stream, "ktile")
+                extra[name + "_ktile_scales"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                                 for k, v in r.items() if k != "flops"}
+                log(f"{name} on K-tile-major scales: {extra[name + '_ktile_scales']}")
 
     cpu = None
     if not args.only_main:
@@ -311,7 +336,8 @@ def main() -> int:
         "dtype": "mxfp8_e4m3",
         "data": "synthetic (seeded N(0,1), 5% rows x1000, quantised to MXFP8 on the host)",
         "config": {"workload": "MXFP8 GEMM M=N=K=4096, E4M3 + E8M0/32, alpha=0.5, bf16 out, 5% outlier rows",
-                   "M": p["M"], "N": p["N"], "K": p["K"], "out": "bf16", "alpha": 0.5},
+                   "M": p["M"], "N": p["N"], "K": p["K"], "out": "bf16", "alpha": 0.5,
+                   "scale_layout": "row-major" if lay == "linear" else "K-tile-major (packed before timing)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -13,14 +13,17 @@ import ctypes
 import os
 
 __all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_nvfp4_f16",
-           "FORMATS", "OUT_DTYPES", "abi_version", "packed_strides", "Problem", "PROBLEM_V1_SIZE"]
+           "FORMATS", "OUT_DTYPES", "SCALE_LAYOUTS", "abi_version", "packed_strides", "Problem", "PROBLEM_V1_SIZE",
+           "pack_scales", "scales_ktile_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsg.so")
 
 FORMATS = {"mxfp8": 1, "nvfp4": 2}
 OUT_DTYPES = {"bf16": 1, "f16": 2}
-EPI_BIAS, EPI_SILU = 1, 2
+EPI_BIAS, EPI_SILU, SCALES_KTILE = 1, 2, 4
+SCALE_LAYOUTS = ("linear", "ktile")  # row-major [rows][K/block], or K-tile-major (BSG_SCALES_KTILE)
+SCALE_BLOCK = {"mxfp8": 32, "nvfp4": 16}
 
 STATUS = {0: "BSG_OK", 1: "BSG_ERR_NULL", 2: "BSG_ERR_SHAPE", 3: "BSG_ERR_UNSUPPORTED", 4: "BSG_ERR_ALIGN",
           5: "BSG_ERR_DEVICE", 6: "BSG_ERR_HIP", 7: "BSG_ERR_ALLOC", 8: "BSG_ERR_ABI"}
@@ -48,10 +51,19 @@ class Problem(ctypes.Structure):
 PROBLEM_V1_SIZE = 48  # sizeof(bsg_problem) of ABI 1, still accepted by bsg_plan_create
 
 
-def packed_strides(fmt: str, M: int, N: int, K: int) -> dict:
+def scales_ktile_bytes(rows: int, codes_per_row: int) -> int:
+    """Bytes of one operand's scales in the K-tile-major layout: ceil(codes / 4) * rows * 4."""
+    return 0 if rows < 1 or codes_per_row < 1 else (codes_per_row + 3) // 4 * rows * 4
+
+
+def packed_strides(fmt: str, M: int, N: int, K: int, scale_layout: str = "linear") -> dict:
     """Byte strides of densely packed batched operands (bias shared by every problem)."""
     elem, blk = (1.0, 32) if fmt == "mxfp8" else (0.5, 16)
-    return dict(a=int(M * K * elem), b=int(N * K * elem), sa=M * K // blk, sb=N * K // blk, bias=0, d=2 * M * N)
+    if scale_layout == "ktile":
+        sa, sb = scales_ktile_bytes(M, K // blk), scales_ktile_bytes(N, K // blk)
+    else:
+        sa, sb = M * K // blk, N * K // blk
+    return dict(a=int(M * K * elem), b=int(N * K * elem), sa=sa, sb=sb, bias=0, d=2 * M * N)
 
 
 class PlanInfo(ctypes.Structure):
@@ -74,6 +86,8 @@ _SIGNATURES = {
     "bsg_last_error": (ctypes.c_char_p, []),
     "bsg_abi_version": (ctypes.c_int, []),
     "bsg_test_decode_nvfp4_f16": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int64, _VP]),
+    "bsg_pack_scales": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, ctypes.c_int64, _VP]),
+    "bsg_scales_ktile_bytes": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int64]),
     "bsg_bench_loop": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_VP), ctypes.c_int,
@@ -134,20 +148,25 @@ class Plan:
 
     batch > 1: that many problems of this shape per call; problem z uses each pointer advanced by
     strides[key] * z bytes (keys a, b, sa, sb, bias, d; default: packed operands, shared bias).
+    scale_layout "ktile": sA and sB in the K-tile-major layout (pack_scales converts).
     """
 
     def __init__(self, fmt: str, M: int, N: int, K: int, out: str = "bf16", bias: bool = False,
-                 silu: bool = False, device: int = -1, batch: int = 1, strides: dict | None = None):
+                 silu: bool = False, device: int = -1, batch: int = 1, strides: dict | None = None,
+                 scale_layout: str = "linear"):
+        if scale_layout not in SCALE_LAYOUTS:
+            raise ValueError(f"scale_layout must be one of {SCALE_LAYOUTS}")
         lib = load_library()
         self._lib = lib
         self._h = None
         self.fmt, self.M, self.N, self.K, self.out, self.bias, self.silu = fmt, M, N, K, out, bias, silu
-        self.batch = batch
-        st = packed_strides(fmt, M, N, K)
+        self.batch, self.scale_layout = batch, scale_layout
+        st = packed_strides(fmt, M, N, K, scale_layout)
         st.update(strides or {})
         self.strides = st
         prob = Problem(ctypes.sizeof(Problem), FORMATS[fmt], OUT_DTYPES[out],
-                       (EPI_BIAS if bias else 0) | (EPI_SILU if silu else 0), M, N, K, device, batch,
+                       (EPI_BIAS if bias else 0) | (EPI_SILU if silu else 0)
+                       | (SCALES_KTILE if scale_layout == "ktile" else 0), M, N, K, device, batch,
                        st["a"], st["b"], st["sa"], st["sb"], st["bias"], st["d"])
         h = _VP()
         _check(lib.bsg_plan_create(ctypes.byref(prob), ctypes.byref(h)))
@@ -213,3 +232,9 @@ def decode_nvfp4_f16(packed, scale_codes, out_f16, n_elements: int, stream=None)
     kernels' routine (packed[k/2] nibble, scale_codes[k/16]); n_elements a multiple of 32."""
     _check(load_library().bsg_test_decode_nvfp4_f16(_ptr(packed), _ptr(scale_codes), _ptr(out_f16), n_elements,
                                                     _stream(stream)))
+
+
+def pack_scales(src, dst, rows: int, codes_per_row: int, stream=None) -> None:
+    """dst (scales_ktile_bytes(rows, codes_per_row) bytes, device) = the K-tile-major layout of the
+    row-major scale codes src [rows][codes_per_row] (device); enqueued on `stream`."""
+    _check(load_library().bsg_pack_scales(_ptr(src), _ptr(dst), rows, codes_per_row, _stream(stream)))

@@ -162,7 +162,7 @@ bsg_status validate(const bsg_problem* p) {
     set_error("unsupported output dtype %d (BF16 or F16 only)", p->out_dtype);
     return BSG_ERR_ABI;
   }
-  if (p->flags & ~(uint32_t)(BSG_EPI_BIAS | BSG_EPI_SILU)) {
+  if (p->flags & ~(uint32_t)(BSG_EPI_BIAS | BSG_EPI_SILU | BSG_SCALES_KTILE)) {
     set_error("unknown flag bits 0x%x", p->flags);
     return BSG_ERR_ABI;
   }
@@ -288,6 +288,7 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   a.K = (int)problem->K;
   a.tiles_m = (int)((problem->M + v.tile_m - 1) / v.tile_m);
   a.tiles_n = (int)((problem->N + v.tile_n - 1) / v.tile_n);
+  a.scale_ktile = (problem->flags & BSG_SCALES_KTILE) ? 1 : 0;
   a.splits = choose_splits(v, (int64_t)a.tiles_m * a.tiles_n * problem->batch, problem->K, g_dev_cus[dev]);
   a.stride_a = problem->stride_a;
   a.stride_b = problem->stride_b;

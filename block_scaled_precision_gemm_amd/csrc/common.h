@@ -29,11 +29,19 @@ struct GemmArgs {
   int M, N, K;
   int tiles_m, tiles_n;   // output tile grid
   int splits;             // split-K factor (1: none)
+  int scale_ktile;        // 0: sA / sB row-major [rows][KB]; 1: K-tile-major [ceil(KB/4)][rows][4]
   float* ws;              // split-K partials [batch][splits][M][N] fp32 (plan-owned), or null
   // Batched problems: grid.z = batch count; batch z uses each pointer advanced by z * its stride
   // (bytes; a stride of 0 shares one matrix / bias vector among all batches).
   int64_t stride_a, stride_b, stride_sa, stride_sb, stride_bias, stride_d;
 };
+
+// Byte offset of scale code `blk` (K block) of operand row `row` in either scale layout: row-major
+// [rows][KB], or K-tile-major, where the 4 codes of K-block group g of every row are stored
+// together: group g, row r, code c at byte (g * rows + r) * 4 + c.
+__device__ __forceinline__ size_t scale_offset(bool ktile, int row, int blk, int rows, int KB) {
+  return ktile ? ((size_t)(blk >> 2) * rows + row) * 4 + (blk & 3) : (size_t)row * KB + blk;
+}
 
 // Move this workgroup's operand, output and workspace pointers to its batch (blockIdx.z).
 __device__ __forceinline__ void select_batch(GemmArgs& p) {

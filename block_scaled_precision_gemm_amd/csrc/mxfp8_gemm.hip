@@ -51,8 +51,6 @@ __global__ __launch_bounds__(256) void mxfp8_direct_kernel(GemmArgs p) {
   const int brow = min(n0 + r, p.N - 1);
   const uint8_t* ap = p.A + (size_t)arow * K + 16 * h;
   const uint8_t* bp = p.B + (size_t)brow * K + 16 * h;
-  const uint8_t* sap = p.sA + (size_t)arow * KB + h;
-  const uint8_t* sbp = p.sB + (size_t)brow * KB + h;
   v16f acc = {};
   for (int k0 = 0; k0 < K; k0 += 64) {
     // block k0/32 always exists; block k0/32 + 1 is missing in the last step when K % 64 == 32
@@ -65,7 +63,9 @@ __global__ __launch_bounds__(256) void mxfp8_direct_kernel(GemmArgs p) {
       b1 = *(const v4i*)(bp + k0 + 32);
     }
     const bool mine = (k0 >> 5) + h < KB;
-    const int sa = mine ? sap[k0 >> 5] : 127, sb = mine ? sbp[k0 >> 5] : 127;
+    const int blk = (k0 >> 5) + h;
+    const int sa = mine ? p.sA[scale_offset(p.scale_ktile, arow, blk, p.M, KB)] : 127;
+    const int sb = mine ? p.sB[scale_offset(p.scale_ktile, brow, blk, p.N, KB)] : 127;
     acc = mfma_mx_e4m3_32x32x64(join(a0, a1), join(b0, b1), acc, sa, sb);
   }
   const int n = n0 + r;

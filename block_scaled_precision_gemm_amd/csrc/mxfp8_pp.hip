@@ -99,11 +99,13 @@ __device__ __forceinline__ void phase_end() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <Out O, bool BIAS, bool SILU>
+template <Out O, bool BIAS, bool SILU, bool KTILE>
 __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
   select_batch(p);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
-  uint8_t* const scale_lds = lds + NS * (A_TILE + B_TILE);  // two buffers: [A rows][16], [B rows][16]
+  // two buffers, each A's 256 rows then B's, 16 scale bytes per row for 512 K: row-major scales as
+  // [row][16] (dword d = K tile d of the 512), K-tile-major scales as [d][row][4]
+  uint8_t* const scale_lds = lds + NS * (A_TILE + B_TILE);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -124,10 +126,15 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
   // 128..255.  Every wave issues the same instruction mix (copies under a branch make the compiler
   // drain them before LDS reads); group 0 copies A's scales, group 1 B's.
   const __amdgpu_buffer_rsrc_t rsT0 = grp == 0 ? rsA : rsB, rsT1 = grp == 0 ? rsB : rsA;
+  // Scale buffer of operand g from the tile's first row.  K-tile-major: up to the array's end (rows
+  // past the operand's last row read other rows' codes, which only reach outputs never stored).
+  const int s_all = grp == 0 ? p.M : p.N, s_first = grp == 0 ? m0 : n0;
+  const uint8_t* const s_base = grp == 0 ? p.sA : p.sB;
   const __amdgpu_buffer_rsrc_t rsS =
-      grp == 0
-          ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.sA + (size_t)m0 * KB), (short)0, m_valid * KB, kRsrcWord3)
-          : __builtin_amdgcn_make_buffer_rsrc((void*)(p.sB + (size_t)n0 * KB), (short)0, n_valid * KB, kRsrcWord3);
+      KTILE ? __builtin_amdgcn_make_buffer_rsrc((void*)(s_base + (size_t)s_first * 4), (short)0,
+                                                KB * s_all - 4 * s_first, kRsrcWord3)
+            : __builtin_amdgcn_make_buffer_rsrc((void*)(s_base + (size_t)s_first * KB), (short)0,
+                                                (grp == 0 ? m_valid : n_valid) * KB, kRsrcWord3);
 
   // Copy plan: a quarter is 128 rows x 128 bytes = 16 instructions of 8 rows; wave 4g + s issues
   // instructions 4s .. 4s+3 (rows 32s + 8q .. +7 of the half).  Lane j writes LDS bytes
@@ -143,8 +150,9 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
   }
   uint8_t* const copy_dst0 = lds + grp * B_BASE + CPW * ws * 1024;              // operand g, rows 0..127
   uint8_t* const copy_dst1 = lds + (1 - grp) * B_BASE + (16 + CPW * ws) * 1024;  // the other, 128..255
-  // Scale plan: wave 4g + s copies rows 64s .. 64s+63 of operand g's scales, 16 bytes each.
-  const uint32_t soff = (uint32_t)(64 * ws + lane) * (uint32_t)KB;
+  // Scale plan: wave 4g + s copies 1 KiB of operand g's scales per 512 K: row-major, rows 64s ..
+  // 64s+63, 16 bytes each; K-tile-major, K tile s of the 512 for all 256 rows (4 rows per lane).
+  const uint32_t soff = KTILE ? 16u * (uint32_t)lane : (uint32_t)(64 * ws + lane) * (uint32_t)KB;
   uint8_t* const sdst = scale_lds + grp * BM * SCALE_BYTES + 64 * ws * SCALE_BYTES;
 
   auto copy_quarter = [&](auto sc, auto pc, int kt) {
@@ -161,7 +169,9 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
   };
   auto copy_scales = [&](auto bc, int batch) {
     constexpr int buf = decltype(bc)::value;
-    const uint32_t k0 = batch < KT * BK / 512 ? (uint32_t)batch * SCALE_BYTES : kOutOfRange;
+    const uint32_t k0 = batch >= KT * BK / 512 ? kOutOfRange
+                        : KTILE                 ? (uint32_t)(4 * batch + ws) * 4u * (uint32_t)s_all
+                                                : (uint32_t)batch * SCALE_BYTES;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, (lds_void*)(sdst + buf * SCALE_BUF), 16, soff, k0, 0, 0);
   };
 
@@ -202,16 +212,20 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
     constexpr int buf = decltype(bc)::value;
     const uint8_t* s = scale_lds + buf * SCALE_BUF;
     const int hs = 8 * h;
+    auto row_scales = [&](const uint8_t* base, int row, uint32_t* out) {
+      if constexpr (KTILE) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const v4i v = *(const v4i*)(s + (WROWS * grp + 32 * i + r) * SCALE_BYTES);
-      sa[i][0] = v[0] >> hs; sa[i][1] = v[1] >> hs; sa[i][2] = v[2] >> hs; sa[i][3] = v[3] >> hs;
-    }
+        for (int d = 0; d < 4; ++d) out[d] = *(const uint32_t*)(base + d * 1024 + row * 4) >> hs;
+      } else {
+        const v4i v = *(const v4i*)(base + row * SCALE_BYTES);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const v4i v = *(const v4i*)(s + BM * SCALE_BYTES + (WCOLS * ws + 32 * j + r) * SCALE_BYTES);
-      sb[j][0] = v[0] >> hs; sb[j][1] = v[1] >> hs; sb[j][2] = v[2] >> hs; sb[j][3] = v[3] >> hs;
-    }
+        for (int d = 0; d < 4; ++d) out[d] = v[d] >> hs;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < TM; ++i) row_scales(s, WROWS * grp + 32 * i + r, sa[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) row_scales(s + BM * SCALE_BYTES, WCOLS * ws + 32 * j + r, sb[j]);
   };
 
   v16f acc[TM][TN];
@@ -338,7 +352,9 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
 template <Out O, bool BIAS, bool SILU>
 hipError_t launch_pp(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
-  return hipLaunchKernel((const void*)&mxfp8_pp_kernel<O, BIAS, SILU>, grid, block, kargs, 0, stream);
+  const void* k = args.scale_ktile ? (const void*)&mxfp8_pp_kernel<O, BIAS, SILU, true>
+                                   : (const void*)&mxfp8_pp_kernel<O, BIAS, SILU, false>;
+  return hipLaunchKernel(k, grid, block, kargs, 0, stream);
 }
 
 #define BSG_MX_PP(O, B, S) \

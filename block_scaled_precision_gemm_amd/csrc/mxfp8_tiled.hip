@@ -141,15 +141,20 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
   const int a_row = (wm * TM * 32 + r) * BK;  // LDS byte offset of this lane's row in row-tile 0
   const int b_row = (wn * TN * 32 + r) * BK;
 
-  // scale pointers: one dword = the 4 E8M0 codes of a K tile; rows past the edge re-read a valid row
+  // scale pointers: one dword = the 4 E8M0 codes of a K tile, dword kt * step of a row's pointer
+  // (row-major: consecutive dwords; K-tile-major: one dword per row per K tile); rows past the edge
+  // re-read a valid row
   const uint32_t* sa_ptr[TM];
   const uint32_t* sb_ptr[TN];
+  const int sa_step = p.scale_ktile ? p.M : 1, sb_step = p.scale_ktile ? p.N : 1;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
-    sa_ptr[i] = (const uint32_t*)(p.sA + (size_t)(m0 + min(wm * TM * 32 + 32 * i + r, m_valid - 1)) * KB);
+    sa_ptr[i] = (const uint32_t*)(p.sA + scale_offset(p.scale_ktile, m0 + min(wm * TM * 32 + 32 * i + r, m_valid - 1),
+                                                       0, p.M, KB));
 #pragma unroll
   for (int j = 0; j < TN; ++j)
-    sb_ptr[j] = (const uint32_t*)(p.sB + (size_t)(n0 + min(wn * TN * 32 + 32 * j + r, n_valid - 1)) * KB);
+    sb_ptr[j] = (const uint32_t*)(p.sB + scale_offset(p.scale_ktile, n0 + min(wn * TN * 32 + 32 * j + r, n_valid - 1),
+                                                       0, p.N, KB));
 
   v16f acc[TM][TN];
 #pragma unroll
@@ -162,9 +167,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
   cpB.issue(rsB, (uint32_t)kt_begin * BK, lds + C::A_TILE);
   uint32_t sa_next[TM], sb_next[TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][kt_begin];
+  for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][(size_t)kt_begin * sa_step];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][kt_begin];
+  for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][(size_t)kt_begin * sb_step];
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     uint32_t sa_cur[TM], sb_cur[TN];
@@ -183,9 +188,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
       cpA.issue(rsA, k1, nxt);
       cpB.issue(rsB, k1, nxt + C::A_TILE);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][kt + 1];
+      for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][(size_t)(kt + 1) * sa_step];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][kt + 1];
+      for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][(size_t)(kt + 1) * sb_step];
     }
     const uint8_t* a_lds = lds + ((kt - kt_begin) & 1) * C::STAGE;
     const uint8_t* b_lds = a_lds + C::A_TILE;

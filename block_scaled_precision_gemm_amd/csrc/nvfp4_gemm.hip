@@ -131,19 +131,29 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // Buffer resources of the shared and private operand rows of this tile (rows past M / N fall
   // outside the range and read as zeros).
   const uint8_t* s_q = SHARED_A ? p.A + (size_t)m0 * KH : p.B + (size_t)n0 * KH;
-  const uint8_t* s_s = SHARED_A ? p.sA + (size_t)m0 * KS : p.sB + (size_t)n0 * KS;
+  // Scale codes: row-major [rows][KS], or K-tile-major (the 4 codes of K tile kt of row r at
+  // (kt * rows + r) * 4): per-lane offsets from the tile's first row plus kt * (4 or 4 * rows).
+  const bool ktile = p.scale_ktile != 0;
+  const int s_all = SHARED_A ? p.M : p.N, p_all = SHARED_A ? p.N : p.M;  // operand rows
+  const int s_first = SHARED_A ? m0 : n0, p_first = SHARED_A ? n0 : m0;
+  const uint32_t s_rowb = ktile ? 4u : KS, s_ktb = ktile ? 4u * (uint32_t)s_all : 4u;
+  const uint32_t p_rowb = ktile ? 4u : KS, p_ktb = ktile ? 4u * (uint32_t)p_all : 4u;
+  const uint8_t* s_s = (SHARED_A ? p.sA : p.sB) + (size_t)s_first * s_rowb;
   const uint8_t* p_q = SHARED_A ? p.B + (size_t)n0 * KH : p.A + (size_t)m0 * KH;
-  const uint8_t* p_s = SHARED_A ? p.sB + (size_t)n0 * KS : p.sA + (size_t)m0 * KS;
+  const uint8_t* p_s = (SHARED_A ? p.sB : p.sA) + (size_t)p_first * p_rowb;
   const int s_rows = SHARED_A ? min(BS, p.M - m0) : min(BS, p.N - n0);
   const int p_rows = SHARED_A ? min(BP, p.N - n0) : min(BP, p.M - m0);
   const __amdgpu_buffer_rsrc_t rs_q =
       __builtin_amdgcn_make_buffer_rsrc((void*)s_q, (short)0, (int)(s_rows * KH), (int)kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rs_s =
-      __builtin_amdgcn_make_buffer_rsrc((void*)s_s, (short)0, (int)(s_rows * KS), (int)kRsrcWord3);
+  // (K-tile-major: the range ends at the array's end; rows past the operand's last row read other
+  // rows' codes, which only reach outputs that are never stored)
+  const uint32_t groups = (KS + 3) >> 2;
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)s_s, (short)0, (int)(ktile ? groups * 4u * (uint32_t)s_all - 4u * (uint32_t)s_first : s_rows * KS), (int)kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rp_q =
       __builtin_amdgcn_make_buffer_rsrc((void*)p_q, (short)0, (int)(p_rows * KH), (int)kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rp_s =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p_s, (short)0, (int)(p_rows * KS), (int)kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rp_s = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p_s, (short)0, (int)(ktile ? groups * 4u * (uint32_t)p_all - 4u * (uint32_t)p_first : p_rows * KS), (int)kRsrcWord3);
 
   // Wave roles: shared half wsh (shared rows 64 wsh .. +64), private quarter wp (private rows
   // 64 wp .. +64); the wave computes those 64 x 64 outputs.
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     const int R = 32 * q + (lane >> 1);
     const int row = q < 4 ? R : R - BS;  // row within its operand's tile rows
     half = data ? (lane & 1) ^ ((R >> 3) & 1) : (lane & 1);
-    off = data ? (uint32_t)row * KH + 16u * half : (uint32_t)row * KS + 2u * half;
+    off = data ? (uint32_t)row * KH + 16u * half : (uint32_t)row * (q < 4 ? s_rowb : p_rowb) + 2u * half;
   };
   uint32_t o_pd, o_ps, o_sd, o_ss;
   int h_unused;
@@ -172,6 +182,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   copy_off(qs, false, o_ss, h_unused);
   const __amdgpu_buffer_rsrc_t r2_q = has_shared ? rs_q : rp_q;
   const __amdgpu_buffer_rsrc_t r2_s = has_shared ? rs_s : rp_s;
+  const uint32_t ktb2 = has_shared ? s_ktb : p_ktb;
   // Copy offsets are loop-invariant (so the compiler's wait bookkeeping stays exact).  The missing
   // half of a final half tile (K % 64 == 32) is still copied -- the next row's first bytes, or zeros
   // past the range for the last row -- and the decode gives it scale code 0, i.e. zero elements.
@@ -179,9 +190,9 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     kt = min(kt, ke - 1);  // past the last tile re-read it (never consumed): uniform load counts
     uint8_t* st = raw + (kt % NR) * RAW_STAGE;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_q, (lds_void*)(st + 1024 * qs), 16, o_sd, (uint32_t)kt * 32u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_s, (lds_void*)(st + RAW_DATA + 256 * qs), 2, o_ss, (uint32_t)kt * 4u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_s, (lds_void*)(st + RAW_DATA + 256 * qs), 2, o_ss, (uint32_t)kt * ktb2, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_q, (lds_void*)(st + 1024 * qp), 16, o_pd, (uint32_t)kt * 32u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_s, (lds_void*)(st + RAW_DATA + 256 * qp), 2, o_ps, (uint32_t)kt * 4u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_s, (lds_void*)(st + RAW_DATA + 256 * qp), 2, o_ps, (uint32_t)kt * p_ktb, 0, 0);
   };
   // Scale codes of half h of K tile kt, or 0 when that half lies past K.
   auto half_scales = [&](uint32_t codes, int kt, int h) -> uint32_t { return kt * BK + 32 * h < K ? codes : 0u; };

@@ -22,7 +22,14 @@
  *   BSG_FMT_NVFP4: A uint8[M][K/2], B uint8[N][K/2] packed E2M1, element 2t
  *                  in the low nibble of byte t; sA uint8[M][K/16],
  *                  sB uint8[N][K/16] E4M3 scale codes, one per 16 K elements.
- * Scale tensors are plain row-major [rows][K/block] (no padding, no swizzle).
+ * Scale tensors are plain row-major [rows][K/block] (no padding, no swizzle)
+ * by default.  With BSG_SCALES_KTILE they use the library's K-tile-major
+ * layout instead (the role of the MXFP8 page's "swizzled" scale layout, which
+ * the page names without defining): with KB = K/block codes per row and
+ * G = ceil(KB/4) groups of 4 codes, code 4g + c of row r (0 <= c < 4) is byte
+ * (g * rows + r) * 4 + c, so one K tile's codes for consecutive rows are
+ * contiguous; codes past KB in the last group are padding (never used).  Size
+ * G * rows * 4 bytes per operand; bsg_pack_scales converts.
  * bias: float[N] (fp32), broadcast over rows.  D: bf16/fp16 [M][N] row-major.
  * All operand pointers are device pointers.
  *
@@ -85,17 +92,18 @@ typedef enum bsg_out_dtype {
   BSG_OUT_F16 = 2
 } bsg_out_dtype;
 
-/* epilogue flags (kEnableBias / kEnableSilu of runNvfp4Gemm) */
+/* problem flags: epilogue (kEnableBias / kEnableSilu of runNvfp4Gemm) and scale layout */
 enum {
-  BSG_EPI_BIAS = 1u << 0, /* add bias[n] after alpha */
-  BSG_EPI_SILU = 1u << 1  /* y = x / (1 + exp(-x)) on x = alpha*acc (+ bias) */
+  BSG_EPI_BIAS = 1u << 0,    /* add bias[n] after alpha */
+  BSG_EPI_SILU = 1u << 1,    /* y = x / (1 + exp(-x)) on x = alpha*acc (+ bias) */
+  BSG_SCALES_KTILE = 1u << 2 /* sA and sB in the K-tile-major layout described above */
 };
 
 typedef struct bsg_problem {
   uint32_t struct_size; /* = sizeof(bsg_problem), or BSG_PROBLEM_V1_SIZE (then batch = 1); else BSG_ERR_ABI */
   int32_t format;       /* bsg_format */
   int32_t out_dtype;    /* bsg_out_dtype */
-  uint32_t flags;       /* BSG_EPI_* */
+  uint32_t flags;       /* BSG_EPI_*, BSG_SCALES_KTILE */
   int64_t M, N, K;      /* M >= 1; N >= 16, N % 16 == 0; K >= 32, K % 32 == 0 (MXFP8) or K % 16 == 0 (NVFP4) */
   int32_t device;       /* HIP device ordinal; -1 = the current device at create time */
   /* Batched GEMM (ABI 2): `batch` independent problems of the same shape in one launch.  Problem z
@@ -148,6 +156,20 @@ bsg_status bsg_plan_destroy(bsg_plan plan);
 
 /* Describe the chosen variant.  info->struct_size must be sizeof(bsg_plan_info). */
 bsg_status bsg_plan_query(bsg_plan plan, bsg_plan_info* info);
+
+/* Convert one operand's scale codes from row-major [rows][codes_per_row] (src) to the K-tile-major
+ * layout of BSG_SCALES_KTILE (dst, bsg_scales_ktile_bytes(rows, codes_per_row) bytes; padding codes
+ * are written as 0), enqueued on `stream` (NULL = the null stream).  src and dst: device pointers to
+ * distinct buffers, dst 4-byte aligned.  For a batch of operands, call once per operand or treat
+ * them as one operand of batch * rows rows only when each operand's rows are contiguous (the
+ * K-tile-major layout interleaves rows per group, so per-operand calls are the general form).
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE (rows or codes_per_row < 1, or the result would exceed 2^31
+ * bytes), BSG_ERR_ALIGN, BSG_ERR_HIP (launch failure). */
+bsg_status bsg_pack_scales(const void* src, void* dst, int64_t rows, int64_t codes_per_row, void* stream);
+
+/* Bytes of one operand's scales in the K-tile-major layout: ceil(codes_per_row / 4) * rows * 4
+ * (0 if an argument is < 1). */
+int64_t bsg_scales_ktile_bytes(int64_t rows, int64_t codes_per_row);
 
 /* Static text for a status code. */
 const char* bsg_status_string(bsg_status s);

@@ -45,7 +45,7 @@ def _create(**kw):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("struct_size", 8, 8), ("format", 3, 8), ("out_dtype", 0, 8), ("flags", 4, 8),
+    ("struct_size", 8, 8), ("format", 3, 8), ("out_dtype", 0, 8), ("flags", 8, 8),
     ("M", 0, 2), ("N", 0, 2), ("K", 0, 2), ("N", 250, 2), ("K", 48, 2), ("M", 1 << 31, 2),
 ])
 def test_plan_create_validation(field, value, status):
@@ -97,6 +97,38 @@ def test_struct_layout_matches_header(tmp_path):
     want = [ctypes.sizeof(P), P.device.offset, P.batch.offset, P.stride_a.offset, P.stride_d.offset,
             ctypes.sizeof(bsg.PlanInfo), bsg.PROBLEM_V1_SIZE]
     assert got == want
+
+
+def test_scale_layout_flag_passes_validation():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    for fmt in (1, 2):
+        st, h = _create(format=fmt, flags=4 | 3)  # K-tile-major scales with bias + SiLU: valid, no device
+        assert st == 5 and not h.value, bsg.load_library().bsg_last_error()
+
+
+@pytest.mark.parametrize("rows,codes", [(1, 1), (1, 4), (3, 5), (257, 128), (130, 66), (0, 4), (4, 0), (-1, 8)])
+def test_scales_ktile_bytes(rows, codes):
+    want = 0 if rows < 1 or codes < 1 else 4 * rows * -(-codes // 4)  # G = ceil(codes / 4) dwords per row
+    assert bsg.load_library().bsg_scales_ktile_bytes(rows, codes) == want == bsg.scales_ktile_bytes(rows, codes)
+
+
+def test_pack_scales_argument_errors():
+    lib = bsg.load_library()
+    assert lib.bsg_pack_scales(None, 16, 4, 4, None) == 1
+    assert lib.bsg_pack_scales(16, None, 4, 4, None) == 1
+    assert lib.bsg_pack_scales(16, 32, 0, 4, None) == 2
+    assert lib.bsg_pack_scales(16, 32, 4, 0, None) == 2
+    assert lib.bsg_pack_scales(16, 32, 1 << 20, 1 << 13, None) == 2  # 2^33 bytes
+    assert lib.bsg_pack_scales(16, 34, 4, 4, None) == 4  # dst not 4-byte aligned
+
+
+def test_packed_strides_for_ktile_scales():
+    st = bsg.packed_strides("nvfp4", 3, 16, 96, "ktile")  # 6 codes per row: 2 groups of 4
+    assert st["sa"] == 2 * 3 * 4 and st["sb"] == 2 * 16 * 4
+    st = bsg.packed_strides("mxfp8", 100, 32, 4096, "ktile")
+    assert st["sa"] == 100 * 128 and st["sb"] == 32 * 128  # a multiple of 4 codes: same bytes as row-major
 
 
 def test_nvfp4_k_rules():
