@@ -18,6 +18,9 @@
 // * Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives each XCD a
 //   contiguous range of tiles, walked in groups of 8 tile-rows, so that concurrently resident
 //   workgroups of one XCD share A and B panels in its L2.
+// * Row-major scales with K % 512 == 0 (BULK, 128 x 128 tiles): a row's codes for 4 K tiles are one
+//   aligned 16-byte piece, loaded once per 4 K tiles instead of a dword per K tile (the per-tile
+//   loads touch one cache line per row each time, more line requests than the operand copies).
 // * Split-K (SPLIT, small tile grids): workgroup id = split * tiles + tile; split s covers a
 //   contiguous range of K tiles and writes its fp32 sums to the plan's workspace ws[s][m][n], which
 //   splitk.h's finish kernel adds in split order and finishes (alpha, bias, SiLU, rounding).
@@ -97,7 +100,7 @@ struct CopyPlan {
   }
 };
 
-template <class C, Out O, bool BIAS, bool SILU, bool SPLIT>
+template <class C, Out O, bool BIAS, bool SILU, bool SPLIT, bool BULK>
 __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
   select_batch(p);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
@@ -162,35 +165,60 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (v16f){};
 
+  // BULK: the 16-byte group of 4 K tiles holding tile kt, per row-tile
+  v4i sa_grp[TM], sb_grp[TN];
+  auto load_group = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa_grp[i] = *(const v4i*)(sa_ptr[i] + 4 * g);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb_grp[j] = *(const v4i*)(sb_ptr[j] + 4 * g);
+  };
+
   // prologue: first K tile -> stage 0, its scales -> registers
   cpA.issue(rsA, (uint32_t)kt_begin * BK, lds);
   cpB.issue(rsB, (uint32_t)kt_begin * BK, lds + C::A_TILE);
   uint32_t sa_next[TM], sb_next[TN];
+  if constexpr (BULK) {
+    load_group(kt_begin >> 2);
+  } else {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][(size_t)kt_begin * sa_step];
+    for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][(size_t)kt_begin * sa_step];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][(size_t)kt_begin * sb_step];
+    for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][(size_t)kt_begin * sb_step];
+  }
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    uint32_t sa_cur[TM], sb_cur[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sa_cur[i] = sa_next[i];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
     // LDS-DMA copies count in vmcnt only; the barrier does not wait for them, and the compiler waits
     // only before this wave's own LDS reads, so each wave drains its copies of tile kt here: after
     // the barrier the whole tile is in its stage and everyone is done reading the other one.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    uint32_t sa_cur[TM], sb_cur[TN];
+    if constexpr (BULK) {
+      const int u = kt & 3;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa_cur[i] = (uint32_t)sa_grp[i][u];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb_cur[j] = (uint32_t)sb_grp[j][u];
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa_cur[i] = sa_next[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
+    }
     if (kt + 1 < kt_end) {
       uint8_t* nxt = lds + ((kt + 1 - kt_begin) & 1) * C::STAGE;
       const uint32_t k1 = (uint32_t)(kt + 1) * BK;
       cpA.issue(rsA, k1, nxt);
       cpB.issue(rsB, k1, nxt + C::A_TILE);
+      if constexpr (BULK) {
+        if (((kt + 1) & 3) == 0) load_group((kt + 1) >> 2);  // lands before the next barrier
+      } else {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][(size_t)(kt + 1) * sa_step];
+        for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][(size_t)(kt + 1) * sa_step];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][(size_t)(kt + 1) * sb_step];
+        for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][(size_t)(kt + 1) * sb_step];
+      }
     }
     const uint8_t* a_lds = lds + ((kt - kt_begin) & 1) * C::STAGE;
     const uint8_t* b_lds = a_lds + C::A_TILE;
@@ -259,11 +287,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 template <class C, Out O, bool BIAS, bool SILU>
 hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
-  if (args.splits <= 1)
-    return hipLaunchKernel((const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false>, grid, block, kargs, 0, stream);
-  const hipError_t e =
-      hipLaunchKernel((const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true>, grid, block, kargs, 0, stream);
-  if (e != hipSuccess) return e;
+  // bulk scale loads: row-major scales, 16-byte aligned groups of 4 K tiles (128 x 128 tiles only: the
+  // 256 x 256 configuration never sees K % 512 == 0, which goes to the large-shape kernel)
+  // scale buffers and strides must then be 16-byte aligned (the ABI promises 4), checked per call
+  const bool bulk = C::BM == 128 && !args.scale_ktile && args.K % 512 == 0 &&
+                    (((uintptr_t)args.sA | (uintptr_t)args.sB | (uintptr_t)args.stride_sa | (uintptr_t)args.stride_sb) &
+                     15) == 0;
+  const void* k = args.splits <= 1 ? (bulk ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, C::BM == 128>
+                                           : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, false>)
+                                   : (bulk ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, C::BM == 128>
+                                           : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, false>);
+  const hipError_t e = hipLaunchKernel(k, grid, block, kargs, 0, stream);
+  if (e != hipSuccess || args.splits <= 1) return e;
   return launch_splitk_finish<O, BIAS, SILU, 0>(args, grid.z, stream);
 }
 
@@ -282,19 +317,21 @@ using Small = Cfg<128, 128, 2, 2, 16>;  // 4 waves of 64 x 64, for problems with
 
 // Explicit instantiations: taking a kernel template's address only inside another template does not
 // make the compiler emit its host-side launch stub when the template argument is a class type.
-#define BSG_MX_INST(C, SP)                                                            \
-  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, false, SP>(GemmArgs); \
-  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, true, SP>(GemmArgs);  \
-  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, false, SP>(GemmArgs);  \
-  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, true, SP>(GemmArgs);   \
-  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, false, SP>(GemmArgs);  \
-  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, true, SP>(GemmArgs);   \
-  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, false, SP>(GemmArgs);   \
-  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, true, SP>(GemmArgs);
-BSG_MX_INST(Large, false)
-BSG_MX_INST(Large, true)
-BSG_MX_INST(Small, false)
-BSG_MX_INST(Small, true)
+#define BSG_MX_INST(C, SP, BU)                                                            \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, false, SP, BU>(GemmArgs); \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, false, true, SP, BU>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, false, SP, BU>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::BF16, true, true, SP, BU>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, false, SP, BU>(GemmArgs);  \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, true, SP, BU>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, false, SP, BU>(GemmArgs);   \
+  template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, true, SP, BU>(GemmArgs);
+BSG_MX_INST(Large, false, false)
+BSG_MX_INST(Large, true, false)
+BSG_MX_INST(Small, false, false)
+BSG_MX_INST(Small, true, false)
+BSG_MX_INST(Small, false, true)
+BSG_MX_INST(Small, true, true)
 #undef BSG_MX_INST
 
 const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);
