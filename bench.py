@@ -22,6 +22,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-main] [--cali
                        [--scale-layout linear|ktile]
        python bench.py --counters-from FETCH_CSV WRITE_CSV   (records HBM traffic from rocprofv3 passes)
        python bench.py --api-loop N   (N direct calls per workload only, for rocprofv3 --hip-trace)
+       python bench.py --only-workload NAME [--steps K --warmup W]   (one workload only, for
+                      rocprofv3 counter passes; prints its timing, not the benchmark line)
 """
 from __future__ import annotations
 
@@ -246,6 +248,9 @@ def main() -> int:
     ap.add_argument("--api-loop", type=int, metavar="N",
                     help="only run N direct bsg_run calls per workload (NVFP4 256x4096x4096 split-K, MXFP8 "
                          "4096^3) from the native loop, for counting HIP API calls under rocprofv3 --hip-trace")
+    ap.add_argument("--only-workload", metavar="NAME",
+                    help="time one workload only (mxfp8_256, mxfp8_4096, mxfp8_8192_silu, nvfp4_128x8192x8192_silu, "
+                         "nvfp4_256x4096x4096_loop) and print its timing (for profiling)")
     ap.add_argument("--scale-layout", choices=("linear", "ktile"), default="linear",
                     help="scale layout of every workload (default: row-major, the ABI default)")
     ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -269,6 +274,11 @@ def main() -> int:
     stream = torch.cuda.Stream()
     if args.api_loop:
         return api_loop(args.api_loop, stream)
+    if args.only_workload:
+        r = time_gemm(si.workload(args.only_workload), args.steps, args.warmup, stream, args.scale_layout)
+        print(json.dumps({"workload": args.only_workload, "scale_layout": args.scale_layout,
+                          **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}}), flush=True)
+        return 0
 
     log("generating the headline workload (MXFP8 4096^3)")
     p = si.workload("mxfp8_4096")
