@@ -1,4 +1,5 @@
-// MXFP8 block-scaled GEMM, LDS-tiled kernels for gfx950 (the path for K % 128 == 0).
+// MXFP8 block-scaled GEMM, LDS-tiled kernels for gfx950 (every shape the large-shape kernel does not
+// take: fewer than 256 tiles of 256 x 256, or K % 512 != 0; any K % 32 == 0).
 //
 // Same operation as mxfp8_gemm.hip (E4M3 operands with one E8M0 scale per 32 K elements, the
 // mx_float8_t / float_ue8m0_t operands of the nvFuser PR #5736 page), organised for CDNA4:
@@ -15,6 +16,8 @@
 //   chunk from 8 or 16 consecutive rows) then hit distinct banks.
 // * E8M0 scales go straight from global memory to registers, one dword (the 4 blocks of a K tile)
 //   per row and K tile, prefetched one tile ahead.
+// * K % 128 != 0: the last K tile is partial.  Its chunks past K are copied from an out-of-range
+//   offset (zeros) and its missing 32-blocks get scale code 127 (2^0), so they add exact zeros.
 // * Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives each XCD a
 //   contiguous range of tiles, walked in groups of 8 tile-rows, so that concurrently resident
 //   workgroups of one XCD share A and B panels in its L2.
@@ -39,6 +42,7 @@ namespace mxt {
 
 constexpr int BK = 128;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range: the load returns zeros
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -81,27 +85,42 @@ __device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
 template <int COPIES>
 struct CopyPlan {
   uint32_t voff[COPIES];
-  int lds_row0;  // first LDS row of the wave's first instruction (wave-uniform)
+  int kpos[COPIES];  // K offset of the lane's chunk within the tile
+  int lds_row0;      // first LDS row of the wave's first instruction (wave-uniform)
 
   __device__ __forceinline__ void init(int wave, int lane, int ld) {
     lds_row0 = 8 * COPIES * wave;
 #pragma unroll
     for (int q = 0; q < COPIES; ++q) {
       const int R = lds_row0 + 8 * q + (lane >> 3);
-      voff[q] = (uint32_t)R * (uint32_t)ld + 16u * (uint32_t)((lane & 7) ^ swz(R));
+      kpos[q] = 16 * ((lane & 7) ^ swz(R));
+      voff[q] = (uint32_t)R * (uint32_t)ld + (uint32_t)kpos[q];
     }
   }
 
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, uint32_t k0, uint8_t* tile) const {
+  // Copy the K tile at byte k0 of each row; `left` = K - k0.  TAIL (K % 128 != 0): in the last,
+  // partial tile the chunks past K take an out-of-range offset and read as zeros (branch-free: a
+  // select per copy).
+  template <bool TAIL>
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, uint32_t k0, int left, uint8_t* tile) const {
 #pragma unroll
     for (int q = 0; q < COPIES; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (lds_row0 + 8 * q) * BK), 16, voff[q], k0,
-                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + (lds_row0 + 8 * q) * BK), 16,
+                                               TAIL && kpos[q] >= left ? kOutOfRange : voff[q], k0, 0, 0);
   }
 };
 
-template <class C, Out O, bool BIAS, bool SILU, bool SPLIT, bool BULK>
+// Scale handling of a launch (template argument SM):
+//   kScaleTile  one dword per row per K tile (K % 128 == 0; either layout: the layout only sets the
+//               stride between K tiles);
+//   kScaleGroup row-major, K % 512 == 0: one 16-byte group per row per 4 K tiles;
+//   kScaleTail  K % 128 != 0: a partial last K tile (zero-filled chunks; missing blocks' codes 127),
+//               row-major codes read as bytes (rows are not dword-aligned).
+enum : int { kScaleTile = 0, kScaleGroup = 1, kScaleTail = 2 };
+
+template <class C, Out O, bool BIAS, bool SILU, bool SPLIT, int SM>
 __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
+  constexpr bool BULK = SM == kScaleGroup, TAIL = SM == kScaleTail;
   select_batch(p);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
   constexpr int TM = C::TM, TN = C::TN;
@@ -111,7 +130,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
   const int r = lane & 31, h = lane >> 5;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int T = p.tiles_m * p.tiles_n;
-  int bid = blockIdx.x, kt_begin = 0, kt_end = p.K / BK;
+  int bid = blockIdx.x, kt_begin = 0, kt_end = (p.K + BK - 1) / BK;
   if constexpr (SPLIT) {  // split-major ids; split s gets K tiles [s KT / S, (s + 1) KT / S)
     const int s = bid / T;
     bid -= s * T;
@@ -147,17 +166,35 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
   // scale pointers: one dword = the 4 E8M0 codes of a K tile, dword kt * step of a row's pointer
   // (row-major: consecutive dwords; K-tile-major: one dword per row per K tile); rows past the edge
   // re-read a valid row
-  const uint32_t* sa_ptr[TM];
-  const uint32_t* sb_ptr[TN];
-  const int sa_step = p.scale_ktile ? p.M : 1, sb_step = p.scale_ktile ? p.N : 1;
+  size_t sa_row[TM], sb_row[TN];  // byte offset of the row's first code (K tile 0)
 #pragma unroll
   for (int i = 0; i < TM; ++i)
-    sa_ptr[i] = (const uint32_t*)(p.sA + scale_offset(p.scale_ktile, m0 + min(wm * TM * 32 + 32 * i + r, m_valid - 1),
-                                                       0, p.M, KB));
+    sa_row[i] = scale_offset(p.scale_ktile, m0 + min(wm * TM * 32 + 32 * i + r, m_valid - 1), 0, p.M, KB);
 #pragma unroll
   for (int j = 0; j < TN; ++j)
-    sb_ptr[j] = (const uint32_t*)(p.sB + scale_offset(p.scale_ktile, n0 + min(wn * TN * 32 + 32 * j + r, n_valid - 1),
-                                                       0, p.N, KB));
+    sb_row[j] = scale_offset(p.scale_ktile, n0 + min(wn * TN * 32 + 32 * j + r, n_valid - 1), 0, p.N, KB);
+  // Scale word of K tile kt (4 codes, code c in byte c); consecutive K tiles are 4 bytes apart
+  // (row-major) or 4 * rows (K-tile-major).  TAIL: codes of 32-blocks past K become 127 (2^0): their
+  // data are zeros, so they add nothing, whatever the padding holds; row-major codes are read as
+  // bytes, as rows are not dword-aligned when KB % 4 != 0.
+  auto scale_word = [&](const uint8_t* base, size_t row, int rows, int kt) -> uint32_t {
+    const size_t step = p.scale_ktile ? (size_t)rows * 4 : 4;
+    if constexpr (!TAIL) {
+      return *(const uint32_t*)(base + row + (size_t)kt * step);
+    } else {
+      const int blk0 = 4 * kt, valid = KB - blk0;
+      uint32_t w = 0;
+      if (p.scale_ktile) {
+        w = *(const uint32_t*)(base + row + (size_t)kt * step);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (c < valid) w |= (uint32_t)base[row + blk0 + c] << (8 * c);
+      }
+      if (valid < 4) w = (w & ((1u << (8 * valid)) - 1u)) | (0x7F7F7F7Fu << (8 * valid));
+      return w;
+    }
+  };
 
   v16f acc[TM][TN];
 #pragma unroll
@@ -169,22 +206,22 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
   v4i sa_grp[TM], sb_grp[TN];
   auto load_group = [&](int g) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa_grp[i] = *(const v4i*)(sa_ptr[i] + 4 * g);
+    for (int i = 0; i < TM; ++i) sa_grp[i] = *(const v4i*)(p.sA + sa_row[i] + 16 * g);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sb_grp[j] = *(const v4i*)(sb_ptr[j] + 4 * g);
+    for (int j = 0; j < TN; ++j) sb_grp[j] = *(const v4i*)(p.sB + sb_row[j] + 16 * g);
   };
 
   // prologue: first K tile -> stage 0, its scales -> registers
-  cpA.issue(rsA, (uint32_t)kt_begin * BK, lds);
-  cpB.issue(rsB, (uint32_t)kt_begin * BK, lds + C::A_TILE);
+  cpA.template issue<TAIL>(rsA, (uint32_t)kt_begin * BK, K - kt_begin * BK, lds);
+  cpB.template issue<TAIL>(rsB, (uint32_t)kt_begin * BK, K - kt_begin * BK, lds + C::A_TILE);
   uint32_t sa_next[TM], sb_next[TN];
   if constexpr (BULK) {
     load_group(kt_begin >> 2);
   } else {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][(size_t)kt_begin * sa_step];
+    for (int i = 0; i < TM; ++i) sa_next[i] = scale_word(p.sA, sa_row[i], p.M, kt_begin);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][(size_t)kt_begin * sb_step];
+    for (int j = 0; j < TN; ++j) sb_next[j] = scale_word(p.sB, sb_row[j], p.N, kt_begin);
   }
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
@@ -209,15 +246,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
     if (kt + 1 < kt_end) {
       uint8_t* nxt = lds + ((kt + 1 - kt_begin) & 1) * C::STAGE;
       const uint32_t k1 = (uint32_t)(kt + 1) * BK;
-      cpA.issue(rsA, k1, nxt);
-      cpB.issue(rsB, k1, nxt + C::A_TILE);
+      cpA.template issue<TAIL>(rsA, k1, K - (int)k1, nxt);
+      cpB.template issue<TAIL>(rsB, k1, K - (int)k1, nxt + C::A_TILE);
       if constexpr (BULK) {
         if (((kt + 1) & 3) == 0) load_group((kt + 1) >> 2);  // lands before the next barrier
       } else {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sa_next[i] = sa_ptr[i][(size_t)(kt + 1) * sa_step];
+        for (int i = 0; i < TM; ++i) sa_next[i] = scale_word(p.sA, sa_row[i], p.M, kt + 1);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) sb_next[j] = sb_ptr[j][(size_t)(kt + 1) * sb_step];
+        for (int j = 0; j < TN; ++j) sb_next[j] = scale_word(p.sB, sb_row[j], p.N, kt + 1);
       }
     }
     const uint8_t* a_lds = lds + ((kt - kt_begin) & 1) * C::STAGE;
@@ -288,15 +325,22 @@ template <class C, Out O, bool BIAS, bool SILU>
 hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
   // bulk scale loads: row-major scales, 16-byte aligned groups of 4 K tiles (128 x 128 tiles only: the
-  // 256 x 256 configuration never sees K % 512 == 0, which goes to the large-shape kernel)
-  // scale buffers and strides must then be 16-byte aligned (the ABI promises 4), checked per call
+  // 256 x 256 configuration never sees K % 512 == 0, which goes to the large-shape kernel); the scale
+  // buffers and strides must then be 16-byte aligned (the ABI promises 4), checked per call
+  constexpr int kGroupOrTile = C::BM == 128 ? kScaleGroup : kScaleTile;
   const bool bulk = C::BM == 128 && !args.scale_ktile && args.K % 512 == 0 &&
                     (((uintptr_t)args.sA | (uintptr_t)args.sB | (uintptr_t)args.stride_sa | (uintptr_t)args.stride_sb) &
                      15) == 0;
-  const void* k = args.splits <= 1 ? (bulk ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, C::BM == 128>
-                                           : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, false>)
-                                   : (bulk ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, C::BM == 128>
-                                           : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, false>);
+  const int sm = args.K % BK ? kScaleTail : bulk ? kScaleGroup : kScaleTile;
+  const void* k;
+  if (args.splits <= 1)
+    k = sm == kScaleTail    ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleTail>
+        : sm == kScaleGroup ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kGroupOrTile>
+                            : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleTile>;
+  else
+    k = sm == kScaleTail    ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleTail>
+        : sm == kScaleGroup ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kGroupOrTile>
+                            : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleTile>;
   const hipError_t e = hipLaunchKernel(k, grid, block, kargs, 0, stream);
   if (e != hipSuccess || args.splits <= 1) return e;
   return launch_splitk_finish<O, BIAS, SILU, 0>(args, grid.z, stream);
@@ -326,12 +370,16 @@ using Small = Cfg<128, 128, 2, 2, 16>;  // 4 waves of 64 x 64, for problems with
   template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, true, SP, BU>(GemmArgs);   \
   template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, false, SP, BU>(GemmArgs);   \
   template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, true, SP, BU>(GemmArgs);
-BSG_MX_INST(Large, false, false)
-BSG_MX_INST(Large, true, false)
-BSG_MX_INST(Small, false, false)
-BSG_MX_INST(Small, true, false)
-BSG_MX_INST(Small, false, true)
-BSG_MX_INST(Small, true, true)
+BSG_MX_INST(Large, false, kScaleTile)
+BSG_MX_INST(Large, true, kScaleTile)
+BSG_MX_INST(Large, false, kScaleTail)
+BSG_MX_INST(Large, true, kScaleTail)
+BSG_MX_INST(Small, false, kScaleTile)
+BSG_MX_INST(Small, true, kScaleTile)
+BSG_MX_INST(Small, false, kScaleGroup)
+BSG_MX_INST(Small, true, kScaleGroup)
+BSG_MX_INST(Small, false, kScaleTail)
+BSG_MX_INST(Small, true, kScaleTail)
 #undef BSG_MX_INST
 
 const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);

@@ -301,14 +301,50 @@ def test_mxfp8_split_k(shape, epi):
     assert rep["ok"], rep
 
 
+# MXFP8 K % 128 != 0 (K % 32 == 0): the tiled kernels' last K tile is partial -- its chunks past K
+# read as zeros and its missing 32-blocks take scale code 127, so they add exact zeros.  Large
+# (256 x 256) and small (128 x 128) tiles, split and unsplit; short K on few tiles runs the direct
+# kernel (a single partial 64-K step, K = 32).
+MXFP8_KTAIL_SHAPES = [(4096, 4096, 4128), (128, 2048, 4192), (300, 528, 1120), (64, 64, 32), (257, 272, 96),
+                      (1, 16, 4160)]
+
+
+@pytest.mark.parametrize("shape", MXFP8_KTAIL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_mxfp8_k_tail(shape):
+    M, N, K = shape
+    p = si.problem("mxfp8", M, N, K, seed=500 + K % 128 + M, bias=True, silu=True, out="f16", alpha=0.5)
+    plan = make_plan(p)
+    info = plan.info()
+    assert info["variant"].startswith("mxfp8_tiled" if K > 512 else "mxfp8_direct"), info
+    print(f"[plan] {shape} {info['variant']} grid={info['grid']}", flush=True)
+    D = run(p, plan=plan)
+    _full_coverage(D)
+    rows = _band_rows(M, extra=(M - 1,)) if M >= 2048 else np.arange(M)
+    rep = compare(D[rows], reference(p, rows=rows), p["alpha"], p["silu"], p["out"])
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 4128), (128, 1024, 2080)], ids=lambda s: "x".join(map(str, s)))
+def test_mxfp8_k_tail_exact_regime_bit_exact(shape):
+    M, N, K = shape
+    p = _exact_regime_problem("mxfp8", M, N, K, seed=K, out="bf16")
+    D = run(p)
+    assert np.array_equal(D, reference(p)["bits"])
+
+
 def test_mxfp8_split_k_plans():
     # 64 tiles of 128 x 128: four K splits fill the 256 CUs
     info = bsg.Plan("mxfp8", 128, 8192, 8192, out="bf16").info()
     assert info["variant"].startswith("mxfp8_tiled_128x128")
     assert info["grid"][0] == 64 * 4 and info["workspace_bytes"] == 4 * 128 * 8192 * 4
     # at most one split per 4 K tiles of 128
-    info = bsg.Plan("mxfp8", 256, 256, 256, out="bf16").info()
+    info = bsg.Plan("mxfp8", 256, 256, 768, out="bf16").info()
+    assert info["variant"].startswith("mxfp8_tiled_128x128")
     assert info["grid"][0] == 4 and info["workspace_bytes"] == 0
+    # short K on few tiles: the direct kernel (64 x 64 tiles, no LDS pipeline)
+    for shape in ((256, 256, 256), (1024, 1024, 512), (64, 4096, 96)):
+        assert bsg.Plan("mxfp8", *shape, out="bf16").info()["variant"].startswith("mxfp8_direct"), shape
+    assert bsg.Plan("mxfp8", 2048, 2048, 512, out="bf16").info()["variant"].startswith("mxfp8_tiled")
 
 
 def test_mxfp8_split_k_exact_regime_bit_exact_and_graph():

@@ -47,8 +47,8 @@ KTILE_SHAPES = [
     ("mxfp8", (4096, 4096, 512)),   # large-shape ping-pong kernel
     ("mxfp8", (4096, 4096, 384)),   # tiled 256 x 256
     ("mxfp8", (128, 2048, 4096)),   # tiled 128 x 128, split K
-    ("mxfp8", (130, 528, 1056)),    # direct kernel; the last group of 4 codes is half padding
-    ("mxfp8", (100, 80, 160)),      # direct kernel, ragged, 5 codes per row
+    ("mxfp8", (130, 528, 1056)),    # tiled, a partial last K tile; the last group of 4 codes is half padding
+    ("mxfp8", (100, 80, 160)),      # direct kernel (short K), ragged, 5 codes per row
     ("nvfp4", (100, 80, 1056)),     # 128 x 256 tiles (shared A), split, a final half K tile
     ("nvfp4", (128, 1024, 4096)),   # shared A, split
     ("nvfp4", (300, 2048, 1056)),   # 256 x 128 tiles (shared B), ragged M, half K tile
@@ -74,6 +74,28 @@ def test_ktile_scales_match_row_major_and_oracle(fmt, shape):
     assert rep["ok"], rep
     lin_plan.close()
     kt_plan.close()
+
+
+@pytest.mark.parametrize("fmt,shape", [("mxfp8", (130, 528, 1056)), ("mxfp8", (4096, 4096, 4128)),
+                                       ("nvfp4", (100, 80, 1056)), ("nvfp4", (300, 2048, 1056))],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_ktile_padding_codes_are_ignored(fmt, shape):
+    """Padding codes of the last group (K not a multiple of 4 blocks) are never used: NaN codes there
+    (E8M0 0xFF, E4M3 0x7F) give the bits of the zero-padded layout."""
+    M, N, K = shape
+    p = si.problem(fmt, M, N, K, seed=K + M, out="bf16", alpha=0.5)
+    q = _ktile_problem(p)
+    kb = p["sA"].shape[1]
+    assert kb % 4, "a shape whose last group has padding"
+    nan = 0xFF if fmt == "mxfp8" else 0x7F
+    poisoned = dict(q)
+    for key, rows in (("sA", M), ("sB", N)):
+        lay = q[key].copy().reshape(-1, rows, 4)
+        lay[-1, :, kb % 4:] = nan
+        poisoned[key] = lay.reshape(-1)
+    plan = bsg.Plan(fmt, M, N, K, out="bf16", scale_layout="ktile")
+    assert np.array_equal(run(poisoned, plan=plan), run(q, plan=plan))
+    plan.close()
 
 
 @pytest.mark.parametrize("fmt,shape", [("mxfp8", (1024, 1024, 512)), ("nvfp4", (128, 1024, 4096)),
