@@ -24,6 +24,10 @@
 // * Row-major scales with K % 512 == 0 (BULK, 128 x 128 tiles): a row's codes for 4 K tiles are one
 //   aligned 16-byte piece, loaded once per 4 K tiles instead of a dword per K tile (the per-tile
 //   loads touch one cache line per row each time, more line requests than the operand copies).
+// * Epilogue through LDS: with B as the MFMAs' first operand each lane holds 4 consecutive output
+//   columns per group; each wave finishes 32 rows at a time in registers, stages them in its own
+//   padded LDS block and stores 16-byte row pieces (2-byte scattered stores were the largest cost
+//   of short-K shapes).
 // * Split-K (SPLIT, small tile grids): workgroup id = split * tiles + tile; split s covers a
 //   contiguous range of K tiles and writes its fp32 sums to the plan's workspace ws[s][m][n], which
 //   splitk.h's finish kernel adds in split order and finishes (alpha, bias, SiLU, rounding).
@@ -175,8 +179,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
     sb_row[j] = scale_offset(p.scale_ktile, n0 + min(wn * TN * 32 + 32 * j + r, n_valid - 1), 0, p.N, KB);
   // Scale word of K tile kt (4 codes, code c in byte c); consecutive K tiles are 4 bytes apart
   // (row-major) or 4 * rows (K-tile-major).  TAIL: codes of 32-blocks past K become 127 (2^0): their
-  // data are zeros, so they add nothing, whatever the padding holds; row-major codes are read as
-  // bytes, as rows are not dword-aligned when KB % 4 != 0.
+  // data are zeros, so they add nothing, whatever the padding holds.  Row-major rows are then not
+  // dword-aligned (KB % 4 != 0): the codes come from the aligned dword holding the first one and,
+  // only when they run into it, the next dword, joined with a byte-align shift (no load reaches a
+  // dword past the last code needed).
   auto scale_word = [&](const uint8_t* base, size_t row, int rows, int kt) -> uint32_t {
     const size_t step = p.scale_ktile ? (size_t)rows * 4 : 4;
     if constexpr (!TAIL) {
@@ -187,9 +193,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
       if (p.scale_ktile) {
         w = *(const uint32_t*)(base + row + (size_t)kt * step);
       } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (c < valid) w |= (uint32_t)base[row + blk0 + c] << (8 * c);
+        const size_t at = row + blk0;
+        const uint32_t* d = (const uint32_t*)(base + (at & ~(size_t)3));
+        const int sh = (int)(at & 3);
+        const uint32_t lo = d[0];
+        const uint32_t hi = sh + min(valid, 4) > 4 ? d[1] : 0u;
+        w = __builtin_amdgcn_alignbyte(hi, lo, sh);
       }
       if (valid < 4) w = (w & ((1u << (8 * valid)) - 1u)) | (0x7F7F7F7Fu << (8 * valid));
       return w;
@@ -280,44 +289,66 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(af[i], bf[j], acc[i][j], sa[i], sb[j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(bf[j], af[i], acc[i][j], sb[j], sa[i]);
     }
   }
 
-  if constexpr (SPLIT) {  // fp32 partial sums of this K range, unscaled
-    float* ws = p.ws + (size_t)(blockIdx.x / T) * p.M * p.N;
+  // Epilogue, staged through LDS.  B is the MFMAs' first operand, so acc[i][j] holds the transposed
+  // block: lane (r, h) element e is row 32i + r, column 32j + 8(e/4) + 4h + e%4 of the wave's block,
+  // four consecutive columns per e/4.  One pass per row-tile i: the wave finishes its 32 rows in
+  // registers (alpha, bias, SiLU, rounding; split: the raw fp32 sums), writes them to its own padded
+  // LDS block, and reads them back as 16-byte row pieces for the global stores (rows past M and
+  // pieces past N are not stored).
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave is done with both stages
+  constexpr int ES = SPLIT ? 4 : 2;     // bytes per output element
+  constexpr int ECOLS = 32 * TN;        // columns of the wave's block
+  constexpr int EROW = ECOLS * ES + 16;  // padded LDS row, bytes
+  constexpr int PPR = ECOLS * ES / 16;  // 16-byte pieces per row
+  constexpr int RPI = 64 / PPR;         // rows per read-back instruction
+  static_assert(C::WAVES * 32 * EROW <= 2 * C::STAGE && RPI * PPR == 64, "epilogue staging");
+  uint8_t* const eb = lds + wave * 32 * EROW;
+  const int mw = m0 + wm * TM * 32, nw = n0 + wn * TN * 32;
+  const float alpha = SPLIT ? 1.0f : load_alpha(p);
+  uint8_t* const out = SPLIT ? (uint8_t*)(p.ws + (size_t)(blockIdx.x / T) * p.M * p.N) : (uint8_t*)p.D;
+  float bv[TN][4][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = nw + 32 * j + 8 * g + 4 * h + c;
+        bv[j][g][c] = BIAS && n < p.N ? p.bias[n] : 0.0f;
+      }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * TN * 32 + 32 * j + r;
-      if (n >= p.N) continue;
+      const v16f& a = acc[i][j];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * TM * 32 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (m < p.M) ws[(size_t)m * p.N + n] = acc[i][j][e];
+      for (int g = 0; g < 4; ++g) {
+        uint8_t* const dst = eb + r * EROW + (32 * j + 8 * g + 4 * h) * ES;
+        if constexpr (SPLIT) {
+          *(v4f*)dst = (v4f){a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        } else {
+          const uint32_t lo = pack2_out<O>(epi_value<SILU>(a[4 * g + 0], alpha, bv[j][g][0]),
+                                           epi_value<SILU>(a[4 * g + 1], alpha, bv[j][g][1]));
+          const uint32_t hi = pack2_out<O>(epi_value<SILU>(a[4 * g + 2], alpha, bv[j][g][2]),
+                                           epi_value<SILU>(a[4 * g + 3], alpha, bv[j][g][3]));
+          *(uint2*)dst = make_uint2(lo, hi);
         }
       }
     }
-    return;
-  }
-
-  // epilogue
-  const float alpha = load_alpha(p);
-  uint16_t* D = (uint16_t*)p.D;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the block is private to this wave
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + wn * TN * 32 + 32 * j + r;
-    if (n >= p.N) continue;
-    const float bv = BIAS ? p.bias[n] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * TM * 32 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m < p.M) D[(size_t)m * p.N + n] = to_out_bits<O>(epi_value<SILU>(acc[i][j][e], alpha, bv));
-      }
+    for (int q = 0; q < 32 / RPI; ++q) {
+      const int row = RPI * q + lane / PPR, pc = lane % PPR;
+      const v4i v = *(const v4i*)(eb + row * EROW + 16 * pc);
+      const int m = mw + 32 * i + row, n = nw + pc * (16 / ES);
+      if (m < p.M && n < p.N) *(v4i*)(out + ((size_t)m * p.N + n) * ES) = v;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next pass rewrites it
   }
 }
 

@@ -303,8 +303,7 @@ def test_mxfp8_split_k(shape, epi):
 
 # MXFP8 K % 128 != 0 (K % 32 == 0): the tiled kernels' last K tile is partial -- its chunks past K
 # read as zeros and its missing 32-blocks take scale code 127, so they add exact zeros.  Large
-# (256 x 256) and small (128 x 128) tiles, split and unsplit; short K on few tiles runs the direct
-# kernel (a single partial 64-K step, K = 32).
+# (256 x 256) and small (128 x 128) tiles, split and unsplit, a single partial tile (K = 32).
 MXFP8_KTAIL_SHAPES = [(4096, 4096, 4128), (128, 2048, 4192), (300, 528, 1120), (64, 64, 32), (257, 272, 96),
                       (1, 16, 4160)]
 
@@ -315,7 +314,7 @@ def test_mxfp8_k_tail(shape):
     p = si.problem("mxfp8", M, N, K, seed=500 + K % 128 + M, bias=True, silu=True, out="f16", alpha=0.5)
     plan = make_plan(p)
     info = plan.info()
-    assert info["variant"].startswith("mxfp8_tiled" if K > 512 else "mxfp8_direct"), info
+    assert info["variant"].startswith("mxfp8_tiled"), info
     print(f"[plan] {shape} {info['variant']} grid={info['grid']}", flush=True)
     D = run(p, plan=plan)
     _full_coverage(D)
@@ -341,10 +340,9 @@ def test_mxfp8_split_k_plans():
     info = bsg.Plan("mxfp8", 256, 256, 768, out="bf16").info()
     assert info["variant"].startswith("mxfp8_tiled_128x128")
     assert info["grid"][0] == 4 and info["workspace_bytes"] == 0
-    # short K on few tiles: the direct kernel (64 x 64 tiles, no LDS pipeline)
+    # short K: 128 x 128 tiles while 256 x 256 ones would not fill the CUs
     for shape in ((256, 256, 256), (1024, 1024, 512), (64, 4096, 96)):
-        assert bsg.Plan("mxfp8", *shape, out="bf16").info()["variant"].startswith("mxfp8_direct"), shape
-    assert bsg.Plan("mxfp8", 2048, 2048, 512, out="bf16").info()["variant"].startswith("mxfp8_tiled")
+        assert bsg.Plan("mxfp8", *shape, out="bf16").info()["variant"].startswith("mxfp8_tiled_128x128"), shape
 
 
 def test_mxfp8_split_k_exact_regime_bit_exact_and_graph():

@@ -48,7 +48,7 @@ KTILE_SHAPES = [
     ("mxfp8", (4096, 4096, 384)),   # tiled 256 x 256
     ("mxfp8", (128, 2048, 4096)),   # tiled 128 x 128, split K
     ("mxfp8", (130, 528, 1056)),    # tiled, a partial last K tile; the last group of 4 codes is half padding
-    ("mxfp8", (100, 80, 160)),      # direct kernel (short K), ragged, 5 codes per row
+    ("mxfp8", (100, 80, 160)),      # tiled, ragged, 5 codes per row
     ("nvfp4", (100, 80, 1056)),     # 128 x 256 tiles (shared A), split, a final half K tile
     ("nvfp4", (128, 1024, 4096)),   # shared A, split
     ("nvfp4", (300, 2048, 1056)),   # 256 x 128 tiles (shared B), ragged M, half K tile
