@@ -27,12 +27,15 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // Two E4M3 scale codes (bits 7:0 and 15:8 of `sc`) -> fp16 pair (s0 * 2^-8, s1 * 2^-8), exact; a
-// NaN code gives an fp16 NaN.
+// NaN code gives an fp16 NaN.  A byte permute puts code i at bits 8..15 of half i; shifted right by
+// one, its magnitude bits land on fp16 bits 13..7 and its sign stays at bit 15.  The NaN magnitude
+// 0x7F lands on 0x3F80, an fp16 NaN but for bit 14, which the carry of 0x3F80 + 0x80 supplies (for
+// that magnitude only).  Seven VALU operations for the pair.
 __device__ __forceinline__ uint32_t e4m3x2_scale_f16x2(uint32_t sc) {
-  uint32_t r = ((sc & 0x7Fu) << 7) | ((sc & 0x80u) << 8) | ((sc & 0x7F00u) << 15) | ((sc & 0x8000u) << 16);
-  if ((sc & 0x7Fu) == 0x7Fu) r = (r & 0xFFFF0000u) | 0x7E00u;
-  if ((sc & 0x7F00u) == 0x7F00u) r = (r & 0x0000FFFFu) | 0x7E000000u;
-  return r;
+  const uint32_t y = __builtin_amdgcn_perm(0u, sc, 0x010C000Cu);  // (c0 << 8) | (c1 << 24)
+  const uint32_t t = (y >> 1) & 0x3F803F80u;
+  const uint32_t nan = (t + 0x00800080u) & 0x40004000u;
+  return t | nan | (y & 0x80008000u);
 }
 
 // fp16 pair (x.lo, x.lo) and (x.hi, x.hi) of a dword of two fp16.

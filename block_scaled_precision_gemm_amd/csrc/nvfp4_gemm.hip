@@ -186,16 +186,27 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // Copy offsets are loop-invariant (so the compiler's wait bookkeeping stays exact).  The missing
   // half of a final half tile (K % 64 == 32) is still copied -- the next row's first bytes, or zeros
   // past the range for the last row -- and the decode gives it scale code 0, i.e. zero elements.
+  // Ring positions count from the split's first tile, so that the steady-state loop, unrolled by the
+  // ring size, sees every stage and decoded-buffer offset as a constant (immediate LDS offsets).
+  static_assert((NR & (NR - 1)) == 0, "ring size a power of two");
+  auto ring = [&](int kt) -> uint32_t { return (uint32_t)(kt - kb) & (NR - 1); };
   auto copy_tile = [&](int kt) {
     kt = min(kt, ke - 1);  // past the last tile re-read it (never consumed): uniform load counts
-    uint8_t* st = raw + (kt % NR) * RAW_STAGE;
+    uint8_t* st = raw + ring(kt) * RAW_STAGE;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_q, (lds_void*)(st + 1024 * qs), 16, o_sd, (uint32_t)kt * 32u, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_s, (lds_void*)(st + RAW_DATA + 256 * qs), 2, o_ss, (uint32_t)kt * ktb2, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_q, (lds_void*)(st + 1024 * qp), 16, o_pd, (uint32_t)kt * 32u, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_s, (lds_void*)(st + RAW_DATA + 256 * qp), 2, o_ps, (uint32_t)kt * p_ktb, 0, 0);
   };
   // Scale codes of half h of K tile kt, or 0 when that half lies past K.
-  auto half_scales = [&](uint32_t codes, int kt, int h) -> uint32_t { return kt * BK + 32 * h < K ? codes : 0u; };
+  // CHECK: the tile may be the split's last one (prologue and drain loops); the steady-state loop
+  // never reaches it and skips the test.
+  auto half_scales = [&](uint32_t codes, int kt, int h, auto check) -> uint32_t {
+    if constexpr (decltype(check)::value) return kt * BK + 32 * h < K ? codes : 0u;
+    return codes;
+  };
+  using Checked = std::integral_constant<bool, true>;
+  using Unchecked = std::integral_constant<bool, false>;
 
   // Shared decode: thread t takes shared row t/4, quarter t&3 (half (t&3)/2, 8 bytes = one scale
   // block), and writes its two decoded pieces 4h + 2 sub + {0, 1}.
@@ -206,12 +217,12 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 #pragma unroll
   for (int d = 0; d < 2; ++d)
     sd_out[d] = (uint32_t)(128 * sd_row + (((4 * sd_h + 2 * sd_sub + d) ^ ((sd_row >> 1) & 7)) << 4));
-  auto decode_shared = [&](int kt) {
-    const uint8_t* st = raw + (kt % NR) * RAW_STAGE;
-    uint8_t* out = dec + (kt & 1) * DEC_STAGE;
+  auto decode_shared = [&](int kt, auto check) {
+    const uint8_t* st = raw + ring(kt) * RAW_STAGE;
+    uint8_t* out = dec + (ring(kt) & 1) * DEC_STAGE;
     const v4i q4 = *(const v4i*)(st + sd_raw);  // the whole half; this thread uses 8 of its 16 bytes
     const uint2 q = sd_sub ? make_uint2((uint32_t)q4[2], (uint32_t)q4[3]) : make_uint2((uint32_t)q4[0], (uint32_t)q4[1]);
-    const uint32_t s = e4m3x2_scale_f16x2(half_scales(*(const uint32_t*)(st + sd_scale), kt, sd_h));
+    const uint32_t s = e4m3x2_scale_f16x2(half_scales(*(const uint32_t*)(st + sd_scale), kt, sd_h, check));
     const uint32_t s2 = sd_sub ? f16x2_splat_hi(s) : f16x2_splat_lo(s);
     *(v4i*)(out + sd_out[0]) = e2m1x8_scaled_f16x8(q.x, s2);
     *(v4i*)(out + sd_out[1]) = e2m1x8_scaled_f16x8(q.y, s2);
@@ -241,16 +252,16 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 
   // One K tile: tile kt+1's shared rows are decoded into the other decoded buffer; tile kt's private
   // rows are decoded into registers slice by slice, one slice ahead of the MFMAs that use them.
-  auto step = [&](int kt) {
-    decode_shared(kt + 1);  // past the last tile: stale bytes into a buffer nobody reads
-    const uint8_t* st = raw + (kt % NR) * RAW_STAGE;
-    const uint8_t* dst = dec + (kt & 1) * DEC_STAGE;
+  auto step = [&](int kt, auto check) {
+    decode_shared(kt + 1, check);  // past the last tile: stale bytes into a buffer nobody reads
+    const uint8_t* st = raw + ring(kt) * RAW_STAGE;
+    const uint8_t* dst = dec + (ring(kt) & 1) * DEC_STAGE;
     v4i pq[TP];
     uint32_t ps[TP][2];
 #pragma unroll
     for (int j = 0; j < TP; ++j) {
       pq[j] = *(const v4i*)(st + pf_raw[j]);
-      const uint32_t s = e4m3x2_scale_f16x2(half_scales(*(const uint32_t*)(st + pf_scale[j]), kt, hl));
+      const uint32_t s = e4m3x2_scale_f16x2(half_scales(*(const uint32_t*)(st + pf_scale[j]), kt, hl, check));
       ps[j][0] = f16x2_splat_lo(s);
       ps[j][1] = f16x2_splat_hi(s);
     }
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   for (int i = 0; i < DIST; ++i) copy_tile(kb + i);
   wait_copies<(DIST - 1) * COPIES>();
   lds_barrier();  // every wave's copies of tile kb have landed
-  decode_shared(kb);
+  decode_shared(kb, Checked{});
   wait_copies<(DIST - 2) * COPIES>();
   lds_barrier();  // tile kb decoded, tile kb+1 landed
   // Steady state: step kt issues tile kt+DIST's copies, computes tile kt and decodes tile kt+1's
@@ -289,16 +300,26 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // (tiles kt+3 .. kt+DIST may stay in flight).  Raw stages in use: kt .. kt+DIST: NR = DIST + 1.
   int kt = kb;
 #pragma unroll 1
+  for (; kt + NR - 1 + DIST < ke; kt += NR) {
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+      copy_tile(kt + c + DIST);
+      step(kt + c, Unchecked{});
+      wait_copies<(DIST - 2) * COPIES>();
+      lds_barrier();
+    }
+  }
+#pragma unroll 1
   for (; kt + DIST < ke; ++kt) {
     copy_tile(kt + DIST);
-    step(kt);
+    step(kt, Unchecked{});
     wait_copies<(DIST - 2) * COPIES>();
     lds_barrier();
   }
   // Last DIST tiles: nothing left to copy.  Leaves no copy in flight past the end of the kernel.
 #pragma unroll 1
   for (; kt < ke; ++kt) {
-    step(kt);
+    step(kt, Checked{});
     wait_copies<0>();
     lds_barrier();
   }
