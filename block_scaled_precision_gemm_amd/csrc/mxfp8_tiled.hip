@@ -50,17 +50,24 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int BM_, int BN_, int WM_, int WN_, int MAX_SPLITS_>
+template <int BM_, int BN_, int WM_, int WN_, int MAX_SPLITS_, int NS_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MAX_SPLITS = MAX_SPLITS_;
+  static constexpr int NS = NS_;  // LDS stages: copies run NS - 1 K tiles ahead
   static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
   static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
   static constexpr int A_TILE = BM * BK, B_TILE = BN * BK, STAGE = A_TILE + B_TILE;
   static constexpr int A_COPIES = BM / 8 / WAVES, B_COPIES = BN / 8 / WAVES;  // per wave per K tile
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
   static_assert(A_COPIES * 8 * WAVES == BM && B_COPIES * 8 * WAVES == BN, "copy split");
-  static_assert(2 * STAGE <= 160 * 1024, "LDS");
+  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS");
+  static constexpr int COPIES = A_COPIES + B_COPIES;
 };
+
+using Large = Cfg<256, 256, 2, 4, 1, 2>;    // 8 waves of 128 x 64 (enough tiles to fill the chip: no split)
+using Small = Cfg<128, 128, 2, 2, 16, 2>;   // 4 waves of 64 x 64, for problems with few large tiles
+using Small3 = Cfg<128, 128, 2, 2, 16, 3>;  // the same with a third stage (twice the bytes in flight per
+                                            // CU), for K ranges of 8 K tiles or more
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -126,7 +133,7 @@ template <class C, Out O, bool BIAS, bool SILU, bool SPLIT, int SM>
 __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
   constexpr bool BULK = SM == kScaleGroup, TAIL = SM == kScaleTail;
   select_batch(p);
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NS * C::STAGE];
   constexpr int TM = C::TM, TN = C::TN;
 
   const int lane = threadIdx.x & 63;
@@ -220,24 +227,48 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
     for (int j = 0; j < TN; ++j) sb_grp[j] = *(const v4i*)(p.sB + sb_row[j] + 16 * g);
   };
 
-  // prologue: first K tile -> stage 0, its scales -> registers
-  cpA.template issue<TAIL>(rsA, (uint32_t)kt_begin * BK, K - kt_begin * BK, lds);
-  cpB.template issue<TAIL>(rsB, (uint32_t)kt_begin * BK, K - kt_begin * BK, lds + C::A_TILE);
+  // Copies of K tile t into its ring stage; with three stages, tiles past the split's range are
+  // issued with an out-of-range offset (zeros, no traffic), so every iteration issues the same
+  // number of copies and a fixed vmcnt proves a tile has landed.
+  auto stage_of = [&](int t) { return lds + ((t - kt_begin) % C::NS) * C::STAGE; };
+  auto issue_tile = [&](int t) {
+    const bool real = t < kt_end;
+    const uint32_t k0 = real ? (uint32_t)t * BK : kOutOfRange;
+    const int left = real ? K - t * BK : 0;
+    cpA.template issue<TAIL>(rsA, k0, left, stage_of(t));
+    cpB.template issue<TAIL>(rsB, k0, left, stage_of(t) + C::A_TILE);
+  };
   uint32_t sa_next[TM], sb_next[TN];
-  if constexpr (BULK) {
-    load_group(kt_begin >> 2);
+  auto load_scales = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa_next[i] = scale_word(p.sA, sa_row[i], p.M, t);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb_next[j] = scale_word(p.sB, sb_row[j], p.N, t);
+  };
+
+  // prologue: the first NS - 1 K tiles -> stages 0 .., the first tile's scales -> registers
+  if constexpr (BULK) load_group(kt_begin >> 2);
+  else load_scales(kt_begin);
+  if constexpr (C::NS == 2) {
+    cpA.template issue<TAIL>(rsA, (uint32_t)kt_begin * BK, K - kt_begin * BK, lds);
+    cpB.template issue<TAIL>(rsB, (uint32_t)kt_begin * BK, K - kt_begin * BK, lds + C::A_TILE);
   } else {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa_next[i] = scale_word(p.sA, sa_row[i], p.M, kt_begin);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sb_next[j] = scale_word(p.sB, sb_row[j], p.N, kt_begin);
+    for (int t = 0; t < C::NS - 1; ++t) issue_tile(kt_begin + t);
   }
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     // LDS-DMA copies count in vmcnt only; the barrier does not wait for them, and the compiler waits
     // only before this wave's own LDS reads, so each wave drains its copies of tile kt here: after
-    // the barrier the whole tile is in its stage and everyone is done reading the other one.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the barrier the whole tile is in its stage and everyone is done reading the stage that the
+    // next copies overwrite.  Three stages: the copies of tile kt+1 (the last COPIES memory
+    // instructions issued) may stay in flight.
+    if constexpr (C::NS == 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      static_assert(C::NS == 3 && C::COPIES < 64, "one tile in flight at the barrier");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::COPIES) : "memory");
+    }
     __syncthreads();
     uint32_t sa_cur[TM], sb_cur[TN];
     if constexpr (BULK) {
@@ -252,7 +283,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 #pragma unroll
       for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
     }
-    if (kt + 1 < kt_end) {
+    if constexpr (C::NS == 3) {
+      // next tile's scales first, then tile kt+2's copies (into the stage tile kt-1 used)
+      if constexpr (BULK) {
+        if (((kt + 1) & 3) == 0 && kt + 1 < kt_end) load_group((kt + 1) >> 2);
+      } else {
+        load_scales(min(kt + 1, kt_end - 1));
+      }
+      // keep the scale loads here, a whole K tile ahead of their use (left to itself the scheduler
+      // sinks them below the MFMAs, and the next barrier then waits out their latency)
+      __builtin_amdgcn_sched_barrier(0);
+      issue_tile(kt + 2);
+    } else if (kt + 1 < kt_end) {
       uint8_t* nxt = lds + ((kt + 1 - kt_begin) & 1) * C::STAGE;
       const uint32_t k1 = (uint32_t)(kt + 1) * BK;
       cpA.template issue<TAIL>(rsA, k1, K - (int)k1, nxt);
@@ -266,7 +308,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
         for (int j = 0; j < TN; ++j) sb_next[j] = scale_word(p.sB, sb_row[j], p.N, kt + 1);
       }
     }
-    const uint8_t* a_lds = lds + ((kt - kt_begin) & 1) * C::STAGE;
+    const uint8_t* a_lds = stage_of(kt);
     const uint8_t* b_lds = a_lds + C::A_TILE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -306,7 +348,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
   constexpr int EROW = ECOLS * ES + 16;  // padded LDS row, bytes
   constexpr int PPR = ECOLS * ES / 16;  // 16-byte pieces per row
   constexpr int RPI = 64 / PPR;         // rows per read-back instruction
-  static_assert(C::WAVES * 32 * EROW <= 2 * C::STAGE && RPI * PPR == 64, "epilogue staging");
+  static_assert(C::WAVES * 32 * EROW <= C::NS * C::STAGE && RPI * PPR == 64, "epilogue staging");
   uint8_t* const eb = lds + wave * 32 * EROW;
   const int mw = m0 + wm * TM * 32, nw = n0 + wn * TN * 32;
   const float alpha = SPLIT ? 1.0f : load_alpha(p);
@@ -352,33 +394,44 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
   }
 }
 
+// The kernel of one configuration for a launch's scale mode and split.
+template <class C, Out O, bool BIAS, bool SILU>
+const void* tiled_kernel_for(int sm, bool split) {
+  constexpr int kGroupOrTile = C::BM == 128 ? kScaleGroup : kScaleTile;
+  if (!split)
+    return sm == kScaleTail    ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleTail>
+           : sm == kScaleGroup ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kGroupOrTile>
+                               : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleTile>;
+  return sm == kScaleTail    ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleTail>
+         : sm == kScaleGroup ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kGroupOrTile>
+                             : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleTile>;
+}
+
 template <class C, Out O, bool BIAS, bool SILU>
 hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
   // bulk scale loads: row-major scales, 16-byte aligned groups of 4 K tiles (128 x 128 tiles only: the
   // 256 x 256 configuration never sees K % 512 == 0, which goes to the large-shape kernel); the scale
   // buffers and strides must then be 16-byte aligned (the ABI promises 4), checked per call
-  constexpr int kGroupOrTile = C::BM == 128 ? kScaleGroup : kScaleTile;
   const bool bulk = C::BM == 128 && !args.scale_ktile && args.K % 512 == 0 &&
                     (((uintptr_t)args.sA | (uintptr_t)args.sB | (uintptr_t)args.stride_sa | (uintptr_t)args.stride_sb) &
                      15) == 0;
   const int sm = args.K % BK ? kScaleTail : bulk ? kScaleGroup : kScaleTile;
-  const void* k;
-  if (args.splits <= 1)
-    k = sm == kScaleTail    ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleTail>
-        : sm == kScaleGroup ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kGroupOrTile>
-                            : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleTile>;
-  else
-    k = sm == kScaleTail    ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleTail>
-        : sm == kScaleGroup ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kGroupOrTile>
-                            : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleTile>;
+  const bool split = args.splits > 1;
+  // 128 x 128 tiles, split K: three LDS stages (two K tiles in flight) when each workgroup runs at
+  // least 8 K tiles.  Split plans are the under-filled grids whose workgroups stream long B panels
+  // from HBM with little reuse (128x8192x8192: 24.2 -> 23.2 us); unsplit grids (2048^3: 14.4 vs
+  // 15.2 us) and short K ranges (256^3: 4.3 vs 4.7 us) are faster with two.
+  const int tiles_per_wg = (args.K + BK - 1) / BK / args.splits;
+  const void* k = C::BM == 128 && split && tiles_per_wg >= 8 ? tiled_kernel_for<Small3, O, BIAS, SILU>(sm, split)
+                                                             : tiled_kernel_for<C, O, BIAS, SILU>(sm, split);
   const hipError_t e = hipLaunchKernel(k, grid, block, kargs, 0, stream);
-  if (e != hipSuccess || args.splits <= 1) return e;
+  if (e != hipSuccess || !split) return e;
   return launch_splitk_finish<O, BIAS, SILU, 0>(args, grid.z, stream);
 }
 
 #define BSG_MX_TILED(NAME, C, O, B, S) \
-  { NAME, &launch_tiled<C, O, B, S>, C::BM, C::BN, BK, C::THREADS, 2 * C::STAGE, true, C::MAX_SPLITS }
+  { NAME, &launch_tiled<C, O, B, S>, C::BM, C::BN, BK, C::THREADS, C::NS * C::STAGE, true, C::MAX_SPLITS }
 #define BSG_MX_TABLE(NAME, C)                                                                    \
   {                                                                                              \
     BSG_MX_TILED(NAME, C, Out::BF16, false, false), BSG_MX_TILED(NAME, C, Out::BF16, false, true), \
@@ -387,8 +440,6 @@ hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t
     BSG_MX_TILED(NAME, C, Out::F16, true, false), BSG_MX_TILED(NAME, C, Out::F16, true, true)      \
   }
 
-using Large = Cfg<256, 256, 2, 4, 1>;   // 8 waves of 128 x 64 (enough tiles to fill the chip: no split)
-using Small = Cfg<128, 128, 2, 2, 16>;  // 4 waves of 64 x 64, for problems with few large tiles
 
 // Explicit instantiations: taking a kernel template's address only inside another template does not
 // make the compiler emit its host-side launch stub when the template argument is a class type.
@@ -411,6 +462,12 @@ BSG_MX_INST(Small, false, kScaleGroup)
 BSG_MX_INST(Small, true, kScaleGroup)
 BSG_MX_INST(Small, false, kScaleTail)
 BSG_MX_INST(Small, true, kScaleTail)
+BSG_MX_INST(Small3, false, kScaleTile)
+BSG_MX_INST(Small3, true, kScaleTile)
+BSG_MX_INST(Small3, false, kScaleGroup)
+BSG_MX_INST(Small3, true, kScaleGroup)
+BSG_MX_INST(Small3, false, kScaleTail)
+BSG_MX_INST(Small3, true, kScaleTail)
 #undef BSG_MX_INST
 
 const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);
