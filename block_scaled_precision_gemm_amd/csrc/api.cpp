@@ -256,7 +256,7 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   const bsg::Out out = problem->out_dtype == BSG_OUT_F16 ? bsg::Out::F16 : bsg::Out::BF16;
   const bsg::KernelVariant* table = problem->format == BSG_FMT_MXFP8
                                         ? bsg::mxfp8_variants(problem->M, problem->N, problem->K, problem->batch)
-                                        : bsg::nvfp4_variants(problem->M, problem->N, problem->K);
+                                        : bsg::nvfp4_variants(problem->M, problem->N, problem->K, problem->batch);
   if (!table) {
     set_error("no kernel variant covers M=%lld N=%lld K=%lld", (long long)problem->M, (long long)problem->N,
               (long long)problem->K);

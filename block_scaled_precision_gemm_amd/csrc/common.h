@@ -75,7 +75,7 @@ struct KernelVariant {
 const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K, int64_t batch);
 const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N, int64_t batch);
 const KernelVariant* mxfp8_pp_variants();
-const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K);
+const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K, int64_t batch);
 
 inline int variant_index(Out out, bool bias, bool silu) {
   return (out == Out::F16 ? 4 : 0) + (bias ? 2 : 0) + (silu ? 1 : 0);

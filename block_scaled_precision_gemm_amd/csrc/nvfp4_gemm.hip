@@ -53,20 +53,32 @@ namespace bsg {
 namespace nvr {
 
 constexpr int BK = 64;                       // K elements per tile
-constexpr int BS = 128, BP = 256;            // shared / private rows per workgroup tile
-constexpr int THREADS = 512, WAVES = 8;  // two waves per SIMD
+constexpr int THREADS = 512, WAVES = 8;      // two waves per SIMD
 constexpr int DIST = 3, NR = DIST + 1;       // copies run DIST tiles ahead; raw ring stages
-constexpr int ROWS = BS + BP;                // rows copied per K tile
-constexpr int RAW_DATA = ROWS * 32;          // 12 KiB
-constexpr int RAW_STAGE = RAW_DATA + ROWS * 8;  // + scale codes, 8 bytes per row
-constexpr int DEC_STAGE = BS * 128;          // 16 KiB
-constexpr int LDS_BYTES = NR * RAW_STAGE + 2 * DEC_STAGE;
 constexpr int COPIES = 4;                    // buffer_load ... lds per wave per K tile
-constexpr int TS = 2, TP = 2;                // 2 shared x 2 private MFMA blocks (64 x 64) per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr float kRescale = 65536.0f;           // 2^16: undoes the 2^-8 of both fp16 operands
-static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-static_assert(WAVES * 32 * 72 * 4 <= LDS_BYTES, "epilogue staging");
+
+// Tile configuration: BS shared rows (128 or 256) x 256 private rows.  Each wave computes BS/2 shared
+// x 64 private outputs (TS x TP accumulators of 32 x 32).
+template <int BS_>
+struct Cfg {
+  static constexpr int BS = BS_, BP = 256;
+  static constexpr int ROWS = BS + BP;                   // rows copied per K tile
+  static constexpr int RAW_DATA = ROWS * 32;             // packed bytes of a K tile
+  static constexpr int RAW_STAGE = RAW_DATA + ROWS * 8;  // + scale codes, 8 bytes per row
+  static constexpr int DEC_STAGE = BS * 128;             // decoded shared rows (fp16)
+  static constexpr int LDS_BYTES = NR * RAW_STAGE + 2 * DEC_STAGE;
+  static constexpr int TS = BS / 64, TP = 2;
+  static constexpr int NSC = BS / 32;                    // shared data copies (32 rows each)
+  static constexpr int EPI_COLS = 32 * TS;               // columns of a wave's block, B shared
+  static constexpr int EPI_STRIDE = 32 * (TS > TP ? TS : TP) + 8;  // floats; 4 rows = 32 mod 64 banks
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(WAVES * 32 * EPI_STRIDE * 4 <= LDS_BYTES, "epilogue staging");
+  static_assert(BS == 128 || BS == 256, "copy plan");
+};
+using Cfg128 = Cfg<128>;  // 128 x 256 (A shared, small M) or 256 x 128 (B shared)
+using Cfg256 = Cfg<256>;  // 256 x 256, B shared, for grids of at least one tile per CU
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -101,11 +113,13 @@ __device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
   return make_int2(first_m + in_group % gsize, in_group / gsize);
 }
 
-template <bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT>
+template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT>
 __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   select_batch(p);
+  constexpr int BS = CF::BS, BP = CF::BP, TS = CF::TS, TP = CF::TP, NSC = CF::NSC;
+  constexpr int RAW_DATA = CF::RAW_DATA, RAW_STAGE = CF::RAW_STAGE, DEC_STAGE = CF::DEC_STAGE;
   constexpr int BM = SHARED_A ? BS : BP, BN = SHARED_A ? BP : BS;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[CF::LDS_BYTES];
   uint8_t* const raw = lds;
   uint8_t* const dec = lds + NR * RAW_STAGE;
 
@@ -155,24 +169,25 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rp_s = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p_s, (short)0, (int)(ktile ? groups * 4u * (uint32_t)p_all - 4u * (uint32_t)p_first : p_rows * KS), (int)kRsrcWord3);
 
-  // Wave roles: shared half wsh (shared rows 64 wsh .. +64), private quarter wp (private rows
-  // 64 wp .. +64); the wave computes those 64 x 64 outputs.
+  // Wave roles: shared half wsh (shared rows BS/2 wsh .. +BS/2), private quarter wp (private rows
+  // 64 wp .. +64); the wave computes those BS/2 x 64 outputs.
   const int wsh = wave & 1, wp = wave >> 1;
 
-  // Copy plan.  A K tile needs 24 copies: data copies of 32 rows x 32 bytes (lane l: row 32q + l/2,
-  // half (l & 1) ^ ((R >> 3) & 1), 16 bytes at 1 KiB * q + 16 l; q = 0..3 shared, 4..11 private) and
-  // their scale copies (lane l: the 2 codes of that row's half l & 1 into the 4-byte slot at
-  // 256 q + 4 l = 8R + 4 (l & 1)).  Wave w issues copies q2 = w + (w & 4) (shared copies 0..3 for
-  // w < 4; for w >= 4 a repeat of its own private copies, which writes the same bytes to the same
-  // place) and its private copies q = 4 + w: the same four copies in every wave, without branches or
-  // selected LDS addresses (either would make the compiler drain all copies before LDS reads).
-  const int qp = 4 + wave, qs = wave + (wave & 4);
-  const bool has_shared = wave < 4;
+  // Copy plan.  A K tile needs ROWS/32 data copies of 32 rows x 32 bytes (lane l: row 32q + l/2,
+  // half (l & 1) ^ ((R >> 3) & 1), 16 bytes at 1 KiB * q + 16 l; q < NSC shared, the rest private)
+  // and as many scale copies (lane l: the 2 codes of that row's half l & 1 into the 4-byte slot at
+  // 256 q + 4 l = 8R + 4 (l & 1)).  BS = 256: wave w issues shared copy w and private copy 8 + w.
+  // BS = 128: wave w issues copy q2 = w + (w & 4) (shared copies 0..3 for w < 4; for w >= 4 a
+  // repeat of its own private copy, which writes the same bytes to the same place) and private copy
+  // 4 + w.  Either way the same four copies in every wave, without branches or selected LDS
+  // addresses (either would make the compiler drain all copies before LDS reads).
+  const int qp = NSC + wave, qs = NSC == 8 ? wave : wave + (wave & 4);
+  const bool has_shared = qs < NSC;
   auto copy_off = [&](int q, bool data, uint32_t& off, int& half) {
     const int R = 32 * q + (lane >> 1);
-    const int row = q < 4 ? R : R - BS;  // row within its operand's tile rows
+    const int row = q < NSC ? R : R - BS;  // row within its operand's tile rows
     half = data ? (lane & 1) ^ ((R >> 3) & 1) : (lane & 1);
-    off = data ? (uint32_t)row * KH + 16u * half : (uint32_t)row * (q < 4 ? s_rowb : p_rowb) + 2u * half;
+    off = data ? (uint32_t)row * KH + 16u * half : (uint32_t)row * (q < NSC ? s_rowb : p_rowb) + 2u * half;
   };
   uint32_t o_pd, o_ps, o_sd, o_ss;
   int h_unused;
@@ -208,24 +223,35 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   using Checked = std::integral_constant<bool, true>;
   using Unchecked = std::integral_constant<bool, false>;
 
-  // Shared decode: thread t takes shared row t/4, quarter t&3 (half (t&3)/2, 8 bytes = one scale
-  // block), and writes its two decoded pieces 4h + 2 sub + {0, 1}.
-  const int sd_row = tid >> 2, sd_h = (tid >> 1) & 1, sd_sub = tid & 1;
+  // Shared decode.  BS = 128: thread t takes shared row t/4, quarter t&3 (half (t&3)/2, 8 bytes = one
+  // scale block) and writes its two decoded pieces 4h + 2 sub + {0, 1}.  BS = 256: thread t takes
+  // shared row t/2, half t&1 (16 bytes = two scale blocks) and writes pieces 4h + {0, 1, 2, 3}.
+  constexpr int SD_PIECES = BS / 64;  // decoded 16-byte pieces per thread per K tile
+  const int sd_row = BS == 256 ? tid >> 1 : tid >> 2;
+  const int sd_h = BS == 256 ? tid & 1 : (tid >> 1) & 1, sd_sub = BS == 256 ? 0 : tid & 1;
   const uint32_t sd_raw = (uint32_t)(32 * sd_row + 16 * (sd_h ^ ((sd_row >> 3) & 1)));
   const uint32_t sd_scale = (uint32_t)(RAW_DATA + 8 * sd_row + 4 * sd_h);
-  uint32_t sd_out[2];
+  uint32_t sd_out[SD_PIECES];
 #pragma unroll
-  for (int d = 0; d < 2; ++d)
+  for (int d = 0; d < SD_PIECES; ++d)
     sd_out[d] = (uint32_t)(128 * sd_row + (((4 * sd_h + 2 * sd_sub + d) ^ ((sd_row >> 1) & 7)) << 4));
   auto decode_shared = [&](int kt, auto check) {
     const uint8_t* st = raw + ring(kt) * RAW_STAGE;
     uint8_t* out = dec + (ring(kt) & 1) * DEC_STAGE;
-    const v4i q4 = *(const v4i*)(st + sd_raw);  // the whole half; this thread uses 8 of its 16 bytes
-    const uint2 q = sd_sub ? make_uint2((uint32_t)q4[2], (uint32_t)q4[3]) : make_uint2((uint32_t)q4[0], (uint32_t)q4[1]);
-    const uint32_t s = e4m3x2_scale_f16x2(half_scales(*(const uint32_t*)(st + sd_scale), kt, sd_h, check));
-    const uint32_t s2 = sd_sub ? f16x2_splat_hi(s) : f16x2_splat_lo(s);
-    *(v4i*)(out + sd_out[0]) = e2m1x8_scaled_f16x8(q.x, s2);
-    *(v4i*)(out + sd_out[1]) = e2m1x8_scaled_f16x8(q.y, s2);
+    const v4i q4 = *(const v4i*)(st + sd_raw);  // the row's half
+    const uint32_t codes = half_scales(*(const uint32_t*)(st + sd_scale), kt, sd_h, check);
+    if constexpr (BS == 256) {
+      v4i r[4];
+      e2m1x32_scaled_f16(q4, codes, r);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) *(v4i*)(out + sd_out[d]) = r[d];
+    } else {  // 8 of the half's 16 bytes
+      const uint2 q = sd_sub ? make_uint2((uint32_t)q4[2], (uint32_t)q4[3]) : make_uint2((uint32_t)q4[0], (uint32_t)q4[1]);
+      const uint32_t s = e4m3x2_scale_f16x2(codes);
+      const uint32_t s2 = sd_sub ? f16x2_splat_hi(s) : f16x2_splat_lo(s);
+      *(v4i*)(out + sd_out[0]) = e2m1x8_scaled_f16x8(q.x, s2);
+      *(v4i*)(out + sd_out[1]) = e2m1x8_scaled_f16x8(q.y, s2);
+    }
   };
 
   // Fragment addressing.  Private block j: stage row 128 + 64 wp + 32j + r, the lane's half hl.
@@ -237,9 +263,9 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     pf_raw[j] = (uint32_t)(32 * R + 16 * (hl ^ ((R >> 3) & 1)));
     pf_scale[j] = (uint32_t)(RAW_DATA + 8 * R + 4 * hl);
   }
-  // Shared block i, slice s: decoded row 64 wsh + 32i + r, piece 4 hl + s.
-  const uint32_t sf_row = (uint32_t)(128 * (64 * wsh + r32));
-  const int sf_sw = (r32 >> 1) & 7;  // (64 wsh + 32i + r) >> 1 & 7 does not depend on wsh, i
+  // Shared block i, slice s: decoded row BS/2 wsh + 32i + r, piece 4 hl + s.
+  const uint32_t sf_row = (uint32_t)(128 * (BS / 2 * wsh + r32));
+  const int sf_sw = (r32 >> 1) & 7;  // (BS/2 wsh + 32i + r) >> 1 & 7 does not depend on wsh, i
   uint32_t sf_piece[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) sf_piece[s] = (uint32_t)(((4 * hl + s) ^ sf_sw) << 4);
@@ -331,12 +357,14 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // for SHARED_A, else j, i).  Rows are EPI_STRIDE floats apart (4 * 72 = 32 mod 64 banks: the two
   // rows a store instruction touches land on different banks); each lane then reads 4 consecutive
   // columns and the wave stores 4 full rows per instruction.
-  constexpr int EPI_STRIDE = 72;
+  constexpr int EPI_STRIDE = CF::EPI_STRIDE;
+  constexpr int PASSES = SHARED_A ? TS : TP, ECOLS = 32 * (SHARED_A ? TP : TS);
+  constexpr int LPR = ECOLS / 4, RPI = 64 / LPR;  // lanes per row (4 columns each), rows per read
   float* stage = (float*)lds + wave * (32 * EPI_STRIDE);
-  const int mw = m0 + 64 * (SHARED_A ? wsh : wp), nw = n0 + 64 * (SHARED_A ? wp : wsh);
+  const int mw = m0 + (SHARED_A ? BS / 2 * wsh : 64 * wp), nw = n0 + (SHARED_A ? 64 * wp : BS / 2 * wsh);
   const float alpha = load_alpha(p) * kRescale;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < PASSES; ++pass) {
 #pragma unroll
     for (int i = 0; i < TS; ++i)
 #pragma unroll
@@ -348,11 +376,11 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
           stage[(8 * (e >> 2) + 4 * hl + (e & 3)) * EPI_STRIDE + 32 * ni + r32] = acc[i][j][e];
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int c4 = 4 * (lane & 15);
+    const int c4 = 4 * (lane % LPR);
     const int n = nw + c4;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int row = 4 * it + (lane >> 4);
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int row = RPI * it + lane / LPR;
       const int m = mw + 32 * pass + row;
       const v4f v = *(const v4f*)(stage + row * EPI_STRIDE + c4);
       if (m >= p.M || n >= p.N) continue;  // N % 16 == 0: a lane's 4 columns are all in or all out
@@ -371,36 +399,44 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   }
 }
 
-template <bool SHARED_A, Out O, bool BIAS, bool SILU>
+template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU>
 hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
   if (args.splits <= 1)
-    return hipLaunchKernel((const void*)&nvfp4_kernel<SHARED_A, O, BIAS, SILU, false>, grid, block, kargs, 0, stream);
+    return hipLaunchKernel((const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, false>, grid, block, kargs, 0,
+                           stream);
   hipError_t e =
-      hipLaunchKernel((const void*)&nvfp4_kernel<SHARED_A, O, BIAS, SILU, true>, grid, block, kargs, 0, stream);
+      hipLaunchKernel((const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, true>, grid, block, kargs, 0, stream);
   if (e != hipSuccess) return e;
   return launch_splitk_finish<O, BIAS, SILU, 16>(args, grid.z, stream);  // accumulators carry 2^-16
 }
 
-#define BSG_NVR(SA, NAME, O, B, S) \
-  { NAME, &launch<SA, O, B, S>, SA ? BS : BP, SA ? BP : BS, BK, THREADS, (uint32_t)LDS_BYTES, true, 16 }
-#define BSG_NVR_TABLE(SA, NAME)                                                              \
-  {                                                                                           \
-    BSG_NVR(SA, NAME, Out::BF16, false, false), BSG_NVR(SA, NAME, Out::BF16, false, true),    \
-        BSG_NVR(SA, NAME, Out::BF16, true, false), BSG_NVR(SA, NAME, Out::BF16, true, true),  \
-        BSG_NVR(SA, NAME, Out::F16, false, false), BSG_NVR(SA, NAME, Out::F16, false, true),  \
-        BSG_NVR(SA, NAME, Out::F16, true, false), BSG_NVR(SA, NAME, Out::F16, true, true),    \
+#define BSG_NVR(CF, SA, NAME, O, B, S, MAXS)                                                          \
+  { NAME, &launch<CF, SA, O, B, S>, SA ? CF::BS : CF::BP, SA ? CF::BP : CF::BS, BK, THREADS, (uint32_t)CF::LDS_BYTES, \
+    true, MAXS }
+#define BSG_NVR_TABLE(CF, SA, NAME, MAXS)                                                                          \
+  {                                                                                                                 \
+    BSG_NVR(CF, SA, NAME, Out::BF16, false, false, MAXS), BSG_NVR(CF, SA, NAME, Out::BF16, false, true, MAXS),      \
+        BSG_NVR(CF, SA, NAME, Out::BF16, true, false, MAXS), BSG_NVR(CF, SA, NAME, Out::BF16, true, true, MAXS),    \
+        BSG_NVR(CF, SA, NAME, Out::F16, false, false, MAXS), BSG_NVR(CF, SA, NAME, Out::F16, false, true, MAXS),    \
+        BSG_NVR(CF, SA, NAME, Out::F16, true, false, MAXS), BSG_NVR(CF, SA, NAME, Out::F16, true, true, MAXS),      \
   }
-const KernelVariant kSharedA[8] = BSG_NVR_TABLE(true, "nvfp4_128x256_sharedA");
-const KernelVariant kSharedB[8] = BSG_NVR_TABLE(false, "nvfp4_256x128_sharedB");
+const KernelVariant kSharedA[8] = BSG_NVR_TABLE(Cfg128, true, "nvfp4_128x256_sharedA", 16);
+const KernelVariant kSharedB[8] = BSG_NVR_TABLE(Cfg128, false, "nvfp4_256x128_sharedB", 16);
+// 256 x 256 tiles are chosen only when they give every CU a workgroup: never split
+const KernelVariant kSharedB256[8] = BSG_NVR_TABLE(Cfg256, false, "nvfp4_256x256_sharedB", 1);
 #undef BSG_NVR_TABLE
 #undef BSG_NVR
 
 }  // namespace nvr
 
-// One 128-row tile of A (small M): A is the shared side; otherwise B is.
-const KernelVariant* nvfp4_variants(int64_t M, int64_t /*N*/, int64_t /*K*/) {
-  return M <= nvr::BS ? nvr::kSharedA : nvr::kSharedB;
+// One 128-row tile of A (small M): A is the shared side.  Otherwise B is: 256 x 256 tiles (half the
+// decode work per output of 256 x 128, twice the MFMAs per barrier) once they give every CU a
+// workgroup, 256 x 128 tiles (split K when still too few) below that.
+const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t /*K*/, int64_t batch) {
+  if (M <= nvr::Cfg128::BS) return nvr::kSharedA;
+  const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256) * batch;
+  return tiles256 >= 256 ? nvr::kSharedB256 : nvr::kSharedB;
 }
 
 }  // namespace bsg

@@ -57,6 +57,7 @@ def _share(problems, keys):
 @pytest.mark.parametrize("fmt,shape,L", [
     ("mxfp8", (96, 64, 256), 3), ("nvfp4", (96, 64, 256), 3),
     ("mxfp8", (1024, 1024, 512), 16),   # 16 tiles x 16 problems: the large-shape kernel
+    ("nvfp4", (1024, 1024, 512), 16),   # ... and the 256 x 256 NVFP4 kernel
     ("nvfp4", (128, 1024, 4096), 2),    # split-K with one workspace slice per problem
     ("mxfp8", (128, 1024, 4096), 2),
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))

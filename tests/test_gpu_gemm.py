@@ -386,6 +386,42 @@ def test_nvfp4_plan_info():
     assert info["variant"].startswith("nvfp4_128x256_sharedA")
     splits = info["grid"][0] // (8192 // info["tile"][1])
     assert splits > 1 and info["workspace_bytes"] == splits * 128 * 8192 * 4
-    # larger M shares the decoded B tile; enough tiles to fill the chip run unsplit
+    # larger M shares the decoded B tile: 256 x 128 tiles, split when too few ...
+    info = bsg.Plan("nvfp4", 1024, 4096, 4096, out="f16").info()
+    assert info["variant"].startswith("nvfp4_256x128") and info["workspace_bytes"] > 0
+    # ... and 256 x 256 tiles, unsplit, once those alone give every CU a workgroup
     info = bsg.Plan("nvfp4", 4096, 4096, 4096, out="f16").info()
-    assert info["variant"].startswith("nvfp4_256x128") and info["workspace_bytes"] == 0
+    assert info["variant"].startswith("nvfp4_256x256") and info["workspace_bytes"] == 0
+    assert info["grid"][0] == 256
+
+
+# NVFP4 grids of at least one 256 x 256 tile per CU: 256 x 256 tiles (B shared: 256 rows decoded per K
+# tile into LDS; 8 waves of 64 x 128).  Ragged M / N, a final half K tile, every epilogue.
+NVFP4_256_SHAPES = [(4096, 4096, 256), (4000, 4112, 1056), (2048, 8192, 512)]
+
+
+@pytest.mark.parametrize("shape", NVFP4_256_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("epi", ["plain", "bias_silu_f16"])
+def test_nvfp4_256x256(shape, epi):
+    M, N, K = shape
+    plain = epi == "plain"
+    p = si.problem("nvfp4", M, N, K, seed=M + N + K, bias=not plain, silu=not plain,
+                   out="bf16" if plain else "f16", alpha=0.75)
+    plan = make_plan(p)
+    assert plan.info()["variant"].startswith("nvfp4_256x256"), plan.info()
+    D = run(p, plan=plan)
+    _full_coverage(D)
+    rows = _band_rows(M, extra=(M - 1,))
+    rep = compare(D[rows], reference(p, rows=rows), p["alpha"], p["silu"], p["out"])
+    print(f"[parity] nvfp4 {shape} {epi} max_rel={rep['max_rel_err']:.3g}", flush=True)
+    assert rep["ok"], rep
+
+
+def test_nvfp4_256x256_exact_regime_bit_exact():
+    p = _exact_regime_problem("nvfp4", 4096, 4096, 512, seed=41, out="bf16")
+    plan = make_plan(p)
+    assert plan.info()["variant"].startswith("nvfp4_256x256")
+    D = run(p, plan=plan)
+    rows = _band_rows(4096, extra=(4095,))
+    R = reference(p, rows=rows)["bits"]
+    assert np.array_equal(D[rows], R), f"{int((D[rows] != R).sum())} of {R.size} sampled entries differ"

@@ -53,6 +53,7 @@ KTILE_SHAPES = [
     ("nvfp4", (128, 1024, 4096)),   # shared A, split
     ("nvfp4", (300, 2048, 1056)),   # 256 x 128 tiles (shared B), ragged M, half K tile
     ("nvfp4", (640, 4096, 256)),    # shared B, unsplit
+    ("nvfp4", (4096, 4096, 288)),   # 256 x 256 tiles, a final half K tile
 ]
 
 
