@@ -276,10 +276,9 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TP; ++j) acc[i][j] = v16f{};
 
-  // One K tile: tile kt+1's shared rows are decoded into the other decoded buffer; tile kt's private
-  // rows are decoded into registers slice by slice, one slice ahead of the MFMAs that use them.
+  // One K tile: tile kt's private rows are decoded into registers slice by slice, one slice ahead of
+  // the MFMAs that use them; tile kt+1's shared rows go to the other decoded buffer.
   auto step = [&](int kt, auto check) {
-    decode_shared(kt + 1, check);  // past the last tile: stale bytes into a buffer nobody reads
     const uint8_t* st = raw + ring(kt) * RAW_STAGE;
     const uint8_t* dst = dec + (ring(kt) & 1) * DEC_STAGE;
     v4i pq[TP];
@@ -310,6 +309,9 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < TP; ++j)
           acc[i][j] = SHARED_A ? mfma_f16(sf[c][i], pf[c][j], acc[i][j]) : mfma_f16(pf[c][j], sf[c][i], acc[i][j]);
+      // tile kt+1's shared rows, decoded behind the first slice's MFMAs rather than ahead of them
+      // (4096^3: -3%); past the last tile: stale bytes into a buffer nobody reads
+      if (s == 0) decode_shared(kt + 1, check);
     }
   };
 
