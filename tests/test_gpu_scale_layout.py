@@ -125,3 +125,46 @@ def test_ktile_scales_batched(fmt, shape):
         rep = compare(out[z], reference(q), q["alpha"], q["silu"], q["out"])
         assert rep["ok"], (z, rep)
     plan.close()
+
+
+@pytest.mark.parametrize("fmt,shape,L", [
+    ("mxfp8", (128, 2048, 8224), 2),   # split K, three LDS stages, a partial last K tile
+    ("mxfp8", (128, 1024, 4160), 2),   # split K, two stages (4 K tiles per split), partial last tile
+    ("mxfp8", (128, 2048, 8192), 2),   # split K, three stages, whole K tiles
+    ("mxfp8", (512, 512, 4224), 3),    # 128 x 128 tiles, split, K % 512 != 0
+    ("nvfp4", (100, 1024, 4128), 2),   # NVFP4 split with a final half K tile
+], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+@pytest.mark.parametrize("layout", ["linear", "ktile"])
+def test_batched_split_tail_combinations(fmt, shape, L, layout):
+    """Batched split plans across the kernels' K-range paths, on either scale layout: every problem's
+    D passes the oracle, and each equals a single-problem plan of the same kernel."""
+    M, N, K = shape
+    problems = [si.problem(fmt, M, N, K, seed=300 + 7 * z + K % 97, bias=True, silu=True, out="f16", alpha=0.5)
+                for z in range(L)]
+    plan = bsg.Plan(fmt, M, N, K, out="f16", bias=True, silu=True, batch=L, scale_layout=layout)
+    info = plan.info()
+    assert info["workspace_bytes"] > 0, info  # a split plan
+    st = plan.strides
+    pack = ktile_layout if layout == "ktile" else (lambda a: a)
+    cat = lambda key, f=lambda a: a: torch.from_numpy(np.concatenate([np.ascontiguousarray(f(q[key])).reshape(-1)
+                                                                      for q in problems])).cuda()
+    A, B, sA, sB = cat("A"), cat("B"), cat("sA", pack), cat("sB", pack)
+    bias = torch.from_numpy(problems[0]["bias"].astype(np.float32)).cuda()  # stride 0: shared bias
+    for q in problems:
+        q["bias"] = problems[0]["bias"]
+    assert sA.numel() == L * st["sa"] and sB.numel() == L * st["sb"]
+    D = torch.full((L * M * N,), 0x7FFF, dtype=torch.int16, device="cuda")
+    plan.run(A, B, sA, sB, D, alpha=0.5, bias=bias)
+    torch.cuda.synchronize()
+    out = D.cpu().numpy().view(np.uint16).reshape(L, M, N)
+    single = bsg.Plan(fmt, M, N, K, out="f16", bias=True, silu=True, scale_layout=layout)
+    same_kernel = single.info()["variant"] == info["variant"] and single.info()["grid"][:2] == info["grid"][:2]
+    for z, q in enumerate(problems):
+        rep = compare(out[z], reference(q), q["alpha"], q["silu"], q["out"])
+        assert rep["ok"], (z, rep)
+        if same_kernel:
+            qq = dict(q)
+            qq["sA"], qq["sB"] = pack(q["sA"]), pack(q["sB"])
+            assert np.array_equal(out[z], run(qq, plan=single)), f"problem {z}"
+    plan.close()
+    single.close()
