@@ -14,8 +14,9 @@
 // * LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row R is stored at chunk
 //   c ^ f(R), f(R) = (R & 7) ^ ((R >> 3) & 1).  The MFMA fragment reads (ds_read_b128 of one
 //   chunk from 8 or 16 consecutive rows) then hit distinct banks.
-// * E8M0 scales go straight from global memory to registers, one dword (the 4 blocks of a K tile)
-//   per row and K tile, prefetched one tile ahead.
+// * E8M0 scales (4 codes per row per K tile) are copied into LDS with the operands, one 4-byte copy
+//   per row, and read from there (see the scale modes below for the row-major K % 512 == 0 and the
+//   partial-tile cases, which keep them in registers).
 // * K % 128 != 0: the last K tile is partial.  Its chunks past K are copied from an out-of-range
 //   offset (zeros) and its missing 32-blocks get scale code 127 (2^0), so they add exact zeros.
 // * Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives each XCD a
@@ -62,6 +63,8 @@ struct Cfg {
   static_assert(A_COPIES * 8 * WAVES == BM && B_COPIES * 8 * WAVES == BN, "copy split");
   static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS");
   static constexpr int COPIES = A_COPIES + B_COPIES;
+  static constexpr int SSTAGE = (BM + BN) * 4;  // scale codes of a K tile staged in LDS (kScaleLds)
+  static_assert(BM + BN == 64 * WAVES && NS * (STAGE + SSTAGE) <= 160 * 1024, "scale staging");
 };
 
 using Large = Cfg<256, 256, 2, 4, 1, 2>;    // 8 waves of 128 x 64 (enough tiles to fill the chip: no split)
@@ -122,18 +125,25 @@ struct CopyPlan {
 };
 
 // Scale handling of a launch (template argument SM):
-//   kScaleTile  one dword per row per K tile (K % 128 == 0; either layout: the layout only sets the
-//               stride between K tiles);
-//   kScaleGroup row-major, K % 512 == 0: one 16-byte group per row per 4 K tiles;
+//   kScaleLds   K % 128 == 0 (either layout; not the group case): the tile's codes are copied into
+//               LDS with the operands, one 4-byte copy per row and K tile (64 rows per wave), and
+//               read from there.  Per-tile dword loads by every wave that needs a row touched one
+//               cache line per row and wave (4096x4096x4224 row-major: 72.8 -> 62.6 us);
+//   kScaleGroup row-major, K % 512 == 0, 128 x 128 tiles: one 16-byte group per row per 4 K tiles
+//               held in registers;
 //   kScaleTail  K % 128 != 0: a partial last K tile (zero-filled chunks; missing blocks' codes 127),
-//               row-major codes read as bytes (rows are not dword-aligned).
-enum : int { kScaleTile = 0, kScaleGroup = 1, kScaleTail = 2 };
+//               codes loaded per row and K tile (row-major rows are not dword-aligned);
+//   kScaleTile  K-tile-major, three-stage split plans: one dword per row per K tile in registers,
+//               loaded a tile ahead (already one cache line per 32 rows; an LDS round trip at the
+//               head of each short K tile cost 9% at 128x8192x8192).
+enum : int { kScaleLds = 0, kScaleGroup = 1, kScaleTail = 2, kScaleTile = 3 };
 
 template <class C, Out O, bool BIAS, bool SILU, bool SPLIT, int SM>
 __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) {
-  constexpr bool BULK = SM == kScaleGroup, TAIL = SM == kScaleTail;
+  constexpr bool BULK = SM == kScaleGroup, TAIL = SM == kScaleTail, LDSS = SM == kScaleLds;
+  constexpr int TILE_LOADS = C::COPIES + (LDSS ? 1 : 0);  // memory instructions per K tile and wave
   select_batch(p);
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NS * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NS * C::STAGE + (LDSS ? C::NS * C::SSTAGE : 0)];
   constexpr int TM = C::TM, TN = C::TN;
 
   const int lane = threadIdx.x & 63;
@@ -184,32 +194,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 #pragma unroll
   for (int j = 0; j < TN; ++j)
     sb_row[j] = scale_offset(p.scale_ktile, n0 + min(wn * TN * 32 + 32 * j + r, n_valid - 1), 0, p.N, KB);
-  // Scale word of K tile kt (4 codes, code c in byte c); consecutive K tiles are 4 bytes apart
-  // (row-major) or 4 * rows (K-tile-major).  TAIL: codes of 32-blocks past K become 127 (2^0): their
-  // data are zeros, so they add nothing, whatever the padding holds.  Row-major rows are then not
-  // dword-aligned (KB % 4 != 0): the codes come from the aligned dword holding the first one and,
-  // only when they run into it, the next dword, joined with a byte-align shift (no load reaches a
-  // dword past the last code needed).
+  // TAIL: scale word of K tile kt (4 codes, code c in byte c), loaded per row; codes of 32-blocks
+  // past K become 127 (2^0): their data are zeros, so they add nothing, whatever the padding holds.
+  // K-tile-major: the dword at row + 4 kt rows.  Row-major rows are not dword-aligned (KB % 4 != 0):
+  // the codes come from the aligned dword holding the first one and, only when they run into it,
+  // the next dword, joined with a byte-align shift (no load reaches a dword past the last code).
   auto scale_word = [&](const uint8_t* base, size_t row, int rows, int kt) -> uint32_t {
-    const size_t step = p.scale_ktile ? (size_t)rows * 4 : 4;
-    if constexpr (!TAIL) {
-      return *(const uint32_t*)(base + row + (size_t)kt * step);
+    if constexpr (SM == kScaleTile) return *(const uint32_t*)(base + row + (size_t)kt * rows * 4);
+    const int blk0 = 4 * kt, valid = KB - blk0;
+    uint32_t w = 0;
+    if (p.scale_ktile) {
+      w = *(const uint32_t*)(base + row + (size_t)kt * rows * 4);
     } else {
-      const int blk0 = 4 * kt, valid = KB - blk0;
-      uint32_t w = 0;
-      if (p.scale_ktile) {
-        w = *(const uint32_t*)(base + row + (size_t)kt * step);
-      } else {
-        const size_t at = row + blk0;
-        const uint32_t* d = (const uint32_t*)(base + (at & ~(size_t)3));
-        const int sh = (int)(at & 3);
-        const uint32_t lo = d[0];
-        const uint32_t hi = sh + min(valid, 4) > 4 ? d[1] : 0u;
-        w = __builtin_amdgcn_alignbyte(hi, lo, sh);
-      }
-      if (valid < 4) w = (w & ((1u << (8 * valid)) - 1u)) | (0x7F7F7F7Fu << (8 * valid));
-      return w;
+      const size_t at = row + blk0;
+      const uint32_t* d = (const uint32_t*)(base + (at & ~(size_t)3));
+      const int sh = (int)(at & 3);
+      const uint32_t lo = d[0];
+      const uint32_t hi = sh + min(valid, 4) > 4 ? d[1] : 0u;
+      w = __builtin_amdgcn_alignbyte(hi, lo, sh);
     }
+    if (valid < 4) w = (w & ((1u << (8 * valid)) - 1u)) | (0x7F7F7F7Fu << (8 * valid));
+    return w;
   };
 
   v16f acc[TM][TN];
@@ -227,6 +232,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
     for (int j = 0; j < TN; ++j) sb_grp[j] = *(const v4i*)(p.sB + sb_row[j] + 16 * g);
   };
 
+  // LDSS: wave w copies the codes of rows 64w .. 64w+63 of the tile's [A rows | B rows] (4 bytes per
+  // row and K tile; rows past M / N lie outside the buffer range and read as zeros).
+  uint8_t* const sc_lds = lds + C::NS * C::STAGE;
+  auto sc_stage_of = [&](int t) { return sc_lds + ((t - kt_begin) % C::NS) * C::SSTAGE; };
+  const bool s_is_a = 64 * wave < C::BM;  // wave-uniform
+  // Row-major: row r's codes of K tile t at r * KB + 4t; K-tile-major: at 4r + 4t * rows (the range
+  // then ends at the array's end: rows past the operand's last read other rows' codes, which only
+  // reach outputs never stored).
+  const int s_all = s_is_a ? p.M : p.N, s_first = s_is_a ? m0 : n0;
+  const uint32_t s_rowb = p.scale_ktile ? 4u : (uint32_t)KB, s_tb = p.scale_ktile ? 4u * (uint32_t)s_all : 4u;
+  const uint32_t s_range = p.scale_ktile ? (uint32_t)KB * (uint32_t)s_all - 4u * (uint32_t)s_first
+                                         : (uint32_t)(s_is_a ? m_valid : n_valid) * (uint32_t)KB;
+  const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((s_is_a ? p.sA : p.sB) + (size_t)s_first * s_rowb), (short)0, (int)s_range, kRsrcWord3);
+  const uint32_t s_voff = (uint32_t)(64 * wave + lane - (s_is_a ? 0 : C::BM)) * s_rowb;
+  auto issue_scales = [&](int t) {
+    if constexpr (LDSS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, (lds_void*)(sc_stage_of(t) + 256 * wave), 4, s_voff,
+                                               t < kt_end ? (uint32_t)t * s_tb : kOutOfRange, 0, 0);
+  };
+
   // Copies of K tile t into its ring stage; with three stages, tiles past the split's range are
   // issued with an out-of-range offset (zeros, no traffic), so every iteration issues the same
   // number of copies and a fixed vmcnt proves a tile has landed.
@@ -237,6 +263,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
     const int left = real ? K - t * BK : 0;
     cpA.template issue<TAIL>(rsA, k0, left, stage_of(t));
     cpB.template issue<TAIL>(rsB, k0, left, stage_of(t) + C::A_TILE);
+    issue_scales(t);
   };
   uint32_t sa_next[TM], sb_next[TN];
   auto load_scales = [&](int t) {
@@ -248,10 +275,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 
   // prologue: the first NS - 1 K tiles -> stages 0 .., the first tile's scales -> registers
   if constexpr (BULK) load_group(kt_begin >> 2);
-  else load_scales(kt_begin);
+  else if constexpr (!LDSS) load_scales(kt_begin);
   if constexpr (C::NS == 2) {
     cpA.template issue<TAIL>(rsA, (uint32_t)kt_begin * BK, K - kt_begin * BK, lds);
     cpB.template issue<TAIL>(rsB, (uint32_t)kt_begin * BK, K - kt_begin * BK, lds + C::A_TILE);
+    issue_scales(kt_begin);
   } else {
 #pragma unroll
     for (int t = 0; t < C::NS - 1; ++t) issue_tile(kt_begin + t);
@@ -266,12 +294,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
     if constexpr (C::NS == 2) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-      static_assert(C::NS == 3 && C::COPIES < 64, "one tile in flight at the barrier");
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::COPIES) : "memory");
+      static_assert(C::NS == 3 && TILE_LOADS < 64, "one tile in flight at the barrier");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TILE_LOADS) : "memory");
     }
     __syncthreads();
     uint32_t sa_cur[TM], sb_cur[TN];
-    if constexpr (BULK) {
+    if constexpr (LDSS) {
+      const uint8_t* sc = sc_stage_of(kt);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa_cur[i] = *(const uint32_t*)(sc + 4 * (wm * TM * 32 + 32 * i + r));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb_cur[j] = *(const uint32_t*)(sc + 4 * (C::BM + wn * TN * 32 + 32 * j + r));
+    } else if constexpr (BULK) {
       const int u = kt & 3;
 #pragma unroll
       for (int i = 0; i < TM; ++i) sa_cur[i] = (uint32_t)sa_grp[i][u];
@@ -287,7 +321,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
       // next tile's scales first, then tile kt+2's copies (into the stage tile kt-1 used)
       if constexpr (BULK) {
         if (((kt + 1) & 3) == 0 && kt + 1 < kt_end) load_group((kt + 1) >> 2);
-      } else {
+      } else if constexpr (!LDSS) {
         load_scales(min(kt + 1, kt_end - 1));
       }
       // keep the scale loads here, a whole K tile ahead of their use (left to itself the scheduler
@@ -299,9 +333,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
       const uint32_t k1 = (uint32_t)(kt + 1) * BK;
       cpA.template issue<TAIL>(rsA, k1, K - (int)k1, nxt);
       cpB.template issue<TAIL>(rsB, k1, K - (int)k1, nxt + C::A_TILE);
+      issue_scales(kt + 1);
       if constexpr (BULK) {
         if (((kt + 1) & 3) == 0) load_group((kt + 1) >> 2);  // lands before the next barrier
-      } else {
+      } else if constexpr (!LDSS) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) sa_next[i] = scale_word(p.sA, sa_row[i], p.M, kt + 1);
 #pragma unroll
@@ -397,14 +432,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 // The kernel of one configuration for a launch's scale mode and split.
 template <class C, Out O, bool BIAS, bool SILU>
 const void* tiled_kernel_for(int sm, bool split) {
-  constexpr int kGroupOrTile = C::BM == 128 ? kScaleGroup : kScaleTile;
+  constexpr int kGroupOrTile = C::BM == 128 ? kScaleGroup : kScaleLds;  // no group mode for 256 x 256
+  constexpr int kTileOrLds = C::NS == 3 ? kScaleTile : kScaleLds;        // register mode: three stages only
+  if (sm == kScaleTile) return split ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kTileOrLds>
+                                     : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kTileOrLds>;
   if (!split)
     return sm == kScaleTail    ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleTail>
            : sm == kScaleGroup ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kGroupOrTile>
-                               : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleTile>;
+                               : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kScaleLds>;
   return sm == kScaleTail    ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleTail>
          : sm == kScaleGroup ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kGroupOrTile>
-                             : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleTile>;
+                             : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kScaleLds>;
 }
 
 template <class C, Out O, bool BIAS, bool SILU>
@@ -416,15 +454,16 @@ hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t
   const bool bulk = C::BM == 128 && !args.scale_ktile && args.K % 512 == 0 &&
                     (((uintptr_t)args.sA | (uintptr_t)args.sB | (uintptr_t)args.stride_sa | (uintptr_t)args.stride_sb) &
                      15) == 0;
-  const int sm = args.K % BK ? kScaleTail : bulk ? kScaleGroup : kScaleTile;
+  int sm = args.K % BK ? kScaleTail : bulk ? kScaleGroup : kScaleLds;
   const bool split = args.splits > 1;
   // 128 x 128 tiles, split K: three LDS stages (two K tiles in flight) when each workgroup runs at
   // least 8 K tiles.  Split plans are the under-filled grids whose workgroups stream long B panels
   // from HBM with little reuse (128x8192x8192: 24.2 -> 23.2 us); unsplit grids (2048^3: 14.4 vs
   // 15.2 us) and short K ranges (256^3: 4.3 vs 4.7 us) are faster with two.
   const int tiles_per_wg = (args.K + BK - 1) / BK / args.splits;
-  const void* k = C::BM == 128 && split && tiles_per_wg >= 8 ? tiled_kernel_for<Small3, O, BIAS, SILU>(sm, split)
-                                                             : tiled_kernel_for<C, O, BIAS, SILU>(sm, split);
+  const bool three = C::BM == 128 && split && tiles_per_wg >= 8;
+  if (three && sm == kScaleLds && args.scale_ktile) sm = kScaleTile;
+  const void* k = three ? tiled_kernel_for<Small3, O, BIAS, SILU>(sm, split) : tiled_kernel_for<C, O, BIAS, SILU>(sm, split);
   const hipError_t e = hipLaunchKernel(k, grid, block, kargs, 0, stream);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_finish<O, BIAS, SILU, 0>(args, grid.z, stream);
@@ -452,22 +491,24 @@ hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t
   template __global__ void mxfp8_tiled_kernel<C, Out::F16, false, true, SP, BU>(GemmArgs);   \
   template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, false, SP, BU>(GemmArgs);   \
   template __global__ void mxfp8_tiled_kernel<C, Out::F16, true, true, SP, BU>(GemmArgs);
-BSG_MX_INST(Large, false, kScaleTile)
-BSG_MX_INST(Large, true, kScaleTile)
 BSG_MX_INST(Large, false, kScaleTail)
 BSG_MX_INST(Large, true, kScaleTail)
-BSG_MX_INST(Small, false, kScaleTile)
-BSG_MX_INST(Small, true, kScaleTile)
 BSG_MX_INST(Small, false, kScaleGroup)
 BSG_MX_INST(Small, true, kScaleGroup)
 BSG_MX_INST(Small, false, kScaleTail)
 BSG_MX_INST(Small, true, kScaleTail)
-BSG_MX_INST(Small3, false, kScaleTile)
-BSG_MX_INST(Small3, true, kScaleTile)
 BSG_MX_INST(Small3, false, kScaleGroup)
 BSG_MX_INST(Small3, true, kScaleGroup)
 BSG_MX_INST(Small3, false, kScaleTail)
 BSG_MX_INST(Small3, true, kScaleTail)
+BSG_MX_INST(Large, false, kScaleLds)
+BSG_MX_INST(Large, true, kScaleLds)
+BSG_MX_INST(Small, false, kScaleLds)
+BSG_MX_INST(Small, true, kScaleLds)
+BSG_MX_INST(Small3, false, kScaleLds)
+BSG_MX_INST(Small3, true, kScaleLds)
+BSG_MX_INST(Small3, false, kScaleTile)
+BSG_MX_INST(Small3, true, kScaleTile)
 #undef BSG_MX_INST
 
 const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);
