@@ -8,7 +8,8 @@
 //   of D as 32 x 32 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4.  With 8 waves two waves
 //   share each SIMD, so one wave's LDS reads overlap the other's MFMAs.
 // * A and B K-tiles are copied global -> LDS with buffer_load_dwordx4 ... lds (16 bytes per lane,
-//   no register staging) into a two-stage ring, so the copy of tile k+1 runs while the MFMAs consume
+//   no register staging) into a two-stage ring (three stages for split plans of 128 x 128 tiles with
+//   at least 8 K tiles per workgroup), so the copies of the next tiles run while the MFMAs consume
 //   tile k; one workgroup barrier per K tile.  Each lane's buffer offsets are computed once; the K
 //   position is a scalar offset.  Rows past M (or N) lie outside the buffer range and read as 0.
 // * LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row R is stored at chunk

@@ -11,12 +11,13 @@
 //   v_pk_mul_f16 applies s * 2^-8; each MFMA product is the exact dequantised product times 2^-16,
 //   accumulated in fp32, and the epilogue multiplies by alpha * 2^16.
 //
-// Work split.  A workgroup tile has a "shared" side of 128 rows and a "private" side of 256 rows:
-// with SHARED_A the tile is 128 (M) x 256 (N), otherwise 256 (M) x 128 (N).  Eight waves (two per
-// SIMD: one wave alone issues VALU work at about half rate and cannot overlap it with its own MFMAs)
-// each compute 64 shared x 64 private outputs (2 x 2 accumulators of 32 x 32).
-// * The shared operand is decoded once per K tile by all 512 threads (8 bytes = 16 elements = one
-//   scale block each) into a double-buffered fp16 LDS tile, read by the waves as MFMA fragments.
+// Work split.  A workgroup tile has a "shared" side of 128 or 256 rows and a "private" side of 256
+// rows: with SHARED_A the tile is 128 (M) x 256 (N), otherwise 256 (M) x 128 (N) or, for grids of at
+// least one tile per CU, 256 x 256.  Eight waves (two per SIMD: one wave alone issues VALU work at
+// about half rate and cannot overlap it with its own MFMAs) each compute BS/2 shared x 64 private
+// outputs (BS/64 x 2 accumulators of 32 x 32).
+// * The shared operand is decoded once per K tile by all 512 threads (16 or 32 elements each) into a
+//   double-buffered fp16 LDS tile, read by the waves as MFMA fragments.
 // * Each wave decodes its private rows straight into MFMA registers: with the K order inside a
 //   64-element tile permuted so that lane l (r = l % 32, h = l / 32) covers elements 32h .. 32h+31,
 //   one 16-byte chunk per lane per 32-row block holds exactly the four fragments of that block.  The
