@@ -290,13 +290,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
     // LDS-DMA copies count in vmcnt only; the barrier does not wait for them, and the compiler waits
     // only before this wave's own LDS reads, so each wave drains its copies of tile kt here: after
     // the barrier the whole tile is in its stage and everyone is done reading the stage that the
-    // next copies overwrite.  Three stages: the copies of tile kt+1 (the last COPIES memory
-    // instructions issued) may stay in flight.
+    // next copies overwrite.  NS >= 3 stages: the copies of tiles kt+1 .. kt+NS-2 (the last
+    // (NS - 2) * TILE_LOADS memory instructions issued) may stay in flight.
     if constexpr (C::NS == 2) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-      static_assert(C::NS == 3 && TILE_LOADS < 64, "one tile in flight at the barrier");
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TILE_LOADS) : "memory");
+      static_assert((C::NS - 2) * TILE_LOADS < 64, "tiles in flight at the barrier");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * TILE_LOADS) : "memory");
     }
     __syncthreads();
     uint32_t sa_cur[TM], sb_cur[TN];
@@ -318,8 +318,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 #pragma unroll
       for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
     }
-    if constexpr (C::NS == 3) {
-      // next tile's scales first, then tile kt+2's copies (into the stage tile kt-1 used)
+    if constexpr (C::NS >= 3) {
+      // next tile's scales first, then tile kt+NS-1's copies (into the stage tile kt-1 used)
       if constexpr (BULK) {
         if (((kt + 1) & 3) == 0 && kt + 1 < kt_end) load_group((kt + 1) >> 2);
       } else if constexpr (!LDSS) {
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
       // keep the scale loads here, a whole K tile ahead of their use (left to itself the scheduler
       // sinks them below the MFMAs, and the next barrier then waits out their latency)
       __builtin_amdgcn_sched_barrier(0);
-      issue_tile(kt + 2);
+      issue_tile(kt + C::NS - 1);
     } else if (kt + 1 < kt_end) {
       uint8_t* nxt = lds + ((kt + 1 - kt_begin) & 1) * C::STAGE;
       const uint32_t k1 = (uint32_t)(kt + 1) * BK;
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 template <class C, Out O, bool BIAS, bool SILU>
 const void* tiled_kernel_for(int sm, bool split) {
   constexpr int kGroupOrTile = C::BM == 128 ? kScaleGroup : kScaleLds;  // no group mode for 256 x 256
-  constexpr int kTileOrLds = C::NS == 3 ? kScaleTile : kScaleLds;        // register mode: three stages only
+  constexpr int kTileOrLds = C::NS >= 3 ? kScaleTile : kScaleLds;        // register mode: deep rings only
   if (sm == kScaleTile) return split ? (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, true, kTileOrLds>
                                      : (const void*)&mxfp8_tiled_kernel<C, O, BIAS, SILU, false, kTileOrLds>;
   if (!split)
