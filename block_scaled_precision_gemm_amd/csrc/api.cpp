@@ -92,15 +92,30 @@ bsg_status check_device(int dev) {
   return BSG_OK;
 }
 
-// Split-K factor for a kernel that supports it: enough workgroups to give every compute unit one,
-// while each split keeps at least 4 K tiles.
-int choose_splits(const bsg::KernelVariant& v, int64_t tiles, int64_t K, int cus) {
+// Fixed cost of splitting K (microseconds): the finish kernel's launch and ramp.
+constexpr double kFinishUs = 2.4;
+
+// Split-K factor for a kernel that supports it.  Candidates run from 1 to the largest factor that
+// keeps the grid within one workgroup per compute unit (ceil(cus / tiles)), at least 4 K tiles per
+// split and the kernel's maximum; the choice minimises the kernel's cost model
+//   ktile_us * ceil(k_tiles / S) + (S > 1 ? kFinishUs + partial_us_per_mib * S * plane_mib : 0),
+// plane_mib = the fp32 partials of one split (batch x M x N x 4 bytes) in MiB.  A shorter loop per
+// workgroup pays for itself only while it outweighs the partial traffic and the second launch.
+int choose_splits(const bsg::KernelVariant& v, int64_t tiles, int64_t K, double plane_bytes, int cus) {
   if (v.max_splits <= 1 || tiles >= cus) return 1;
   const int64_t k_tiles = (K + v.tile_k - 1) / v.tile_k;
-  int64_t s = (cus + tiles - 1) / tiles;
-  if (s > k_tiles / 4) s = k_tiles / 4;
-  if (s > v.max_splits) s = v.max_splits;
-  return s < 1 ? 1 : (int)s;
+  int64_t s_max = (cus + tiles - 1) / tiles;
+  if (s_max > k_tiles / 4) s_max = k_tiles / 4;
+  if (s_max > v.max_splits) s_max = v.max_splits;
+  const double plane_mib = plane_bytes / (1024.0 * 1024.0);
+  int best = 1;
+  double best_us = v.ktile_us * (double)k_tiles;
+  for (int64_t s = 2; s <= s_max; ++s) {
+    const double us = v.ktile_us * (double)((k_tiles + s - 1) / s) + kFinishUs +
+                      v.partial_us_per_mib * (double)s * plane_mib;
+    if (us < best_us) best_us = us, best = (int)s;
+  }
+  return best;
 }
 
 // hipMalloc / hipFree on `dev`, restoring the caller's current device.
@@ -289,7 +304,8 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   a.tiles_m = (int)((problem->M + v.tile_m - 1) / v.tile_m);
   a.tiles_n = (int)((problem->N + v.tile_n - 1) / v.tile_n);
   a.scale_ktile = (problem->flags & BSG_SCALES_KTILE) ? 1 : 0;
-  a.splits = choose_splits(v, (int64_t)a.tiles_m * a.tiles_n * problem->batch, problem->K, g_dev_cus[dev]);
+  a.splits = choose_splits(v, (int64_t)a.tiles_m * a.tiles_n * problem->batch, problem->K,
+                           4.0 * (double)problem->batch * (double)problem->M * (double)problem->N, g_dev_cus[dev]);
   a.stride_a = problem->stride_a;
   a.stride_b = problem->stride_b;
   a.stride_sa = problem->stride_sa;

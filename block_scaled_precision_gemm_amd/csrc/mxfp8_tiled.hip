@@ -424,7 +424,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
       const int row = RPI * q + lane / PPR, pc = lane % PPR;
       const v4i v = *(const v4i*)(eb + row * EROW + 16 * pc);
       const int m = mw + 32 * i + row, n = nw + pc * (16 / ES);
-      if (m < p.M && n < p.N) *(v4i*)(out + ((size_t)m * p.N + n) * ES) = v;
+      if (m < p.M && n < p.N) {
+        v4i* const dst = (v4i*)(out + ((size_t)m * p.N + n) * ES);
+        if constexpr (SPLIT)
+          __builtin_nontemporal_store(v, dst);  // partials: streaming store, read once by the finish kernel
+        else
+          *dst = v;
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next pass rewrites it
   }
@@ -471,7 +477,8 @@ hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t
 }
 
 #define BSG_MX_TILED(NAME, C, O, B, S) \
-  { NAME, &launch_tiled<C, O, B, S>, C::BM, C::BN, BK, C::THREADS, C::NS * C::STAGE, true, C::MAX_SPLITS }
+  { NAME, &launch_tiled<C, O, B, S>, C::BM, C::BN, BK, C::THREADS, C::NS * C::STAGE, true, C::MAX_SPLITS, \
+    kSplitKtileUs, kSplitPartialUsPerMib }
 #define BSG_MX_TABLE(NAME, C)                                                                    \
   {                                                                                              \
     BSG_MX_TILED(NAME, C, Out::BF16, false, false), BSG_MX_TILED(NAME, C, Out::BF16, false, true), \
@@ -512,6 +519,9 @@ BSG_MX_INST(Small3, false, kScaleTile)
 BSG_MX_INST(Small3, true, kScaleTile)
 #undef BSG_MX_INST
 
+// Split-K cost model of the 128 x 128 kernel (see choose_splits): fitted to split sweeps of shapes
+// with 16 to 64 tiles and 8 to 64 K tiles on MI355X.  The 256 x 256 configuration never splits.
+constexpr float kSplitKtileUs = 0.60f, kSplitPartialUsPerMib = 0.49f;
 const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);
 const KernelVariant kSmall[8] = BSG_MX_TABLE("mxfp8_tiled_128x128x128_w4", Small);
 #undef BSG_MX_TABLE

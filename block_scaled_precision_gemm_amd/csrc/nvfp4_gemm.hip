@@ -388,7 +388,8 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
       const v4f v = *(const v4f*)(stage + row * EPI_STRIDE + c4);
       if (m >= p.M || n >= p.N) continue;  // N % 16 == 0: a lane's 4 columns are all in or all out
       if constexpr (SPLIT) {
-        *(v4f*)(p.ws + (size_t)split * p.M * p.N + (size_t)m * p.N + n) = v;
+        // streaming store: read once, by the finish kernel
+        __builtin_nontemporal_store(v, (v4f*)(p.ws + (size_t)split * p.M * p.N + (size_t)m * p.N + n));
       } else {
         v4f b = {0.f, 0.f, 0.f, 0.f};
         if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
@@ -416,7 +417,7 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
 
 #define BSG_NVR(CF, SA, NAME, O, B, S, MAXS)                                                          \
   { NAME, &launch<CF, SA, O, B, S>, SA ? CF::BS : CF::BP, SA ? CF::BP : CF::BS, BK, THREADS, (uint32_t)CF::LDS_BYTES, \
-    true, MAXS }
+    true, MAXS, kSplitKtileUs, kSplitPartialUsPerMib }
 #define BSG_NVR_TABLE(CF, SA, NAME, MAXS)                                                                          \
   {                                                                                                                 \
     BSG_NVR(CF, SA, NAME, Out::BF16, false, false, MAXS), BSG_NVR(CF, SA, NAME, Out::BF16, false, true, MAXS),      \
@@ -424,6 +425,9 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
         BSG_NVR(CF, SA, NAME, Out::F16, false, false, MAXS), BSG_NVR(CF, SA, NAME, Out::F16, false, true, MAXS),    \
         BSG_NVR(CF, SA, NAME, Out::F16, true, false, MAXS), BSG_NVR(CF, SA, NAME, Out::F16, true, true, MAXS),      \
   }
+// Split-K cost model (see choose_splits): fitted to split sweeps of small-M shapes (M 64..512,
+// N 1024..8192, K 2048..8192) on MI355X.
+constexpr float kSplitKtileUs = 0.66f, kSplitPartialUsPerMib = 0.34f;
 const KernelVariant kSharedA[8] = BSG_NVR_TABLE(Cfg128, true, "nvfp4_128x256_sharedA", 16);
 const KernelVariant kSharedB[8] = BSG_NVR_TABLE(Cfg128, false, "nvfp4_256x128_sharedB", 16);
 // 256 x 256 tiles are chosen only when they give every CU a workgroup: never split

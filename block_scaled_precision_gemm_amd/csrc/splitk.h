@@ -22,8 +22,9 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   const int m = (int)(idx / nq), n = (int)(idx - (int64_t)m * nq) * 4;
   const size_t plane = (size_t)p.M * p.N;
   const float* src = p.ws + (size_t)m * p.N + n;
-  v4f s = *(const v4f*)src;
-  for (int k = 1; k < p.splits; ++k) s += *(const v4f*)(src + k * plane);
+  // streaming loads: every partial is read exactly once
+  v4f s = __builtin_nontemporal_load((const v4f*)src);
+  for (int k = 1; k < p.splits; ++k) s += __builtin_nontemporal_load((const v4f*)(src + k * plane));
   const float alpha = load_alpha(p) * (float)(1u << RESCALE_LOG2);
   v4f b = {0.f, 0.f, 0.f, 0.f};
   if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};  // bias: 4-byte aligned
