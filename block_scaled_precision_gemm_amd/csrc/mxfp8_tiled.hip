@@ -522,6 +522,8 @@ BSG_MX_INST(Small3, true, kScaleTile)
 // Split-K cost model of the 128 x 128 kernel (see choose_splits): fitted to split sweeps of shapes
 // with 16 to 64 tiles and 8 to 64 K tiles on MI355X.  The 256 x 256 configuration never splits.
 constexpr float kSplitKtileUs = 0.60f, kSplitPartialUsPerMib = 0.49f;
+static_assert(Small::MAX_SPLITS <= kMaxFinishSplits && Small3::MAX_SPLITS == Small::MAX_SPLITS,
+              "the finish kernel sums at most kMaxFinishSplits partials");
 const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);
 const KernelVariant kSmall[8] = BSG_MX_TABLE("mxfp8_tiled_128x128x128_w4", Small);
 #undef BSG_MX_TABLE

@@ -428,8 +428,10 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
 // Split-K cost model (see choose_splits): fitted to split sweeps of small-M shapes (M 64..512,
 // N 1024..8192, K 2048..8192) on MI355X.
 constexpr float kSplitKtileUs = 0.66f, kSplitPartialUsPerMib = 0.34f;
-const KernelVariant kSharedA[8] = BSG_NVR_TABLE(Cfg128, true, "nvfp4_128x256_sharedA", 16);
-const KernelVariant kSharedB[8] = BSG_NVR_TABLE(Cfg128, false, "nvfp4_256x128_sharedB", 16);
+constexpr int kMaxSplits = 16;
+static_assert(kMaxSplits <= kMaxFinishSplits, "the finish kernel sums at most kMaxFinishSplits partials");
+const KernelVariant kSharedA[8] = BSG_NVR_TABLE(Cfg128, true, "nvfp4_128x256_sharedA", kMaxSplits);
+const KernelVariant kSharedB[8] = BSG_NVR_TABLE(Cfg128, false, "nvfp4_256x128_sharedB", kMaxSplits);
 // 256 x 256 tiles are chosen only when they give every CU a workgroup: never split
 const KernelVariant kSharedB256[8] = BSG_NVR_TABLE(Cfg256, false, "nvfp4_256x256_sharedB", 1);
 #undef BSG_NVR_TABLE

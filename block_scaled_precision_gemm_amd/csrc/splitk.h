@@ -6,6 +6,12 @@
 // rounding) and writes D.  RESCALE multiplies alpha for kernels whose accumulators carry a known
 // power-of-two factor (the NVFP4 fp16 route: 2^-16).  One thread per 4 consecutive columns
 // (N % 16 == 0); grid.z = batch.
+//
+// LOAD_ALL issues a thread's S partial loads before the first sum: one memory round trip instead of
+// S.  That pays while one partial plane (batch x M x N x 4 bytes, what all threads read per round
+// trip) is smaller than latency x bandwidth (~4 MiB: 0.8 us at ~5 TB/s), where a plane-by-plane
+// pass waits on latency; from there on the plane-by-plane order streams at least as fast (measured:
+// 1-2 MiB planes 5-11% faster with LOAD_ALL, 4 MiB planes 1% slower).
 #pragma once
 
 #include "common.h"
@@ -13,7 +19,10 @@
 
 namespace bsg {
 
-template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2>
+// The largest split factor of any split-capable kernel (KernelVariant::max_splits).
+constexpr int kMaxFinishSplits = 16;
+
+template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, bool LOAD_ALL>
 __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   select_batch(p);
   const int nq = p.N >> 2;
@@ -22,9 +31,21 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   const int m = (int)(idx / nq), n = (int)(idx - (int64_t)m * nq) * 4;
   const size_t plane = (size_t)p.M * p.N;
   const float* src = p.ws + (size_t)m * p.N + n;
-  // streaming loads: every partial is read exactly once
-  v4f s = __builtin_nontemporal_load((const v4f*)src);
-  for (int k = 1; k < p.splits; ++k) s += __builtin_nontemporal_load((const v4f*)(src + k * plane));
+  // streaming loads: every partial is read exactly once; sums in split order either way
+  v4f s;
+  if constexpr (LOAD_ALL) {
+    v4f part[kMaxFinishSplits];
+#pragma unroll
+    for (int k = 0; k < kMaxFinishSplits; ++k)
+      if (k < p.splits) part[k] = __builtin_nontemporal_load((const v4f*)(src + k * plane));
+    s = part[0];
+#pragma unroll
+    for (int k = 1; k < kMaxFinishSplits; ++k)
+      if (k < p.splits) s += part[k];
+  } else {
+    s = __builtin_nontemporal_load((const v4f*)src);
+    for (int k = 1; k < p.splits; ++k) s += __builtin_nontemporal_load((const v4f*)(src + k * plane));
+  }
   const float alpha = load_alpha(p) * (float)(1u << RESCALE_LOG2);
   v4f b = {0.f, 0.f, 0.f, 0.f};
   if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};  // bias: 4-byte aligned
@@ -36,10 +57,13 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
 // Enqueue the finish kernel of a split plan (grid.z of the GEMM launch = batch).
 template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2>
 hipError_t launch_splitk_finish(const GemmArgs& args, unsigned batch, hipStream_t stream) {
+  if (args.splits < 1 || args.splits > kMaxFinishSplits) return hipErrorInvalidValue;
   void* kargs[] = {(void*)&args};
   const int64_t threads = (int64_t)args.M * (args.N >> 2);
-  return hipLaunchKernel((const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2>,
-                         dim3((unsigned)((threads + 255) / 256), 1, batch), dim3(256), kargs, 0, stream);
+  const bool load_all = 16.0 * (double)threads * (double)batch < 4.0 * 1024 * 1024;  // one plane < 4 MiB
+  const void* k = load_all ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, true>
+                           : (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, false>;
+  return hipLaunchKernel(k, dim3((unsigned)((threads + 255) / 256), 1, batch), dim3(256), kargs, 0, stream);
 }
 
 }  // namespace bsg

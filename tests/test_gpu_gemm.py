@@ -340,6 +340,13 @@ def test_mxfp8_split_k_plans():
     info = bsg.Plan("mxfp8", 256, 256, 768, out="bf16").info()
     assert info["variant"].startswith("mxfp8_tiled_128x128")
     assert info["grid"][0] == 4 and info["workspace_bytes"] == 0
+    # 64 tiles of 8 K tiles: a split would save 4 K tiles per workgroup but cost the finish pass and
+    # 8 MiB of partials (measured 11.8 vs 8.2 us unsplit), so the cost model keeps it whole
+    info = bsg.Plan("mxfp8", 1024, 1024, 1024, out="bf16").info()
+    assert info["grid"][0] == 64 and info["workspace_bytes"] == 0
+    # 32 tiles of 32 K tiles: four splits (measured best of 1..4; eight would add partials for no gain)
+    info = bsg.Plan("mxfp8", 512, 1024, 4096, out="bf16").info()
+    assert info["grid"][0] == 32 * 4 and info["workspace_bytes"] == 4 * 512 * 1024 * 4
     # short K: 128 x 128 tiles while 256 x 256 ones would not fill the CUs
     for shape in ((256, 256, 256), (1024, 1024, 512), (64, 4096, 96)):
         assert bsg.Plan("mxfp8", *shape, out="bf16").info()["variant"].startswith("mxfp8_tiled_128x128"), shape
@@ -386,6 +393,12 @@ def test_nvfp4_plan_info():
     assert info["variant"].startswith("nvfp4_128x256_sharedA")
     splits = info["grid"][0] // (8192 // info["tile"][1])
     assert splits > 1 and info["workspace_bytes"] == splits * 128 * 8192 * 4
+    # the looped 256x4096x4096 problem: 32 tiles of 64 K tiles; the cost model stops short of filling
+    # every CU (8 splits) because each further split adds 4 MiB of partials for one K tile less
+    info = bsg.Plan("nvfp4", 256, 4096, 4096, out="bf16").info()
+    splits = info["grid"][0] // 32
+    assert info["variant"].startswith("nvfp4_256x128_sharedB") and 4 <= splits < 8, info
+    assert info["workspace_bytes"] == splits * 256 * 4096 * 4
     # larger M shares the decoded B tile: 256 x 128 tiles, split when too few ...
     info = bsg.Plan("nvfp4", 1024, 4096, 4096, out="f16").info()
     assert info["variant"].startswith("nvfp4_256x128") and info["workspace_bytes"] > 0
