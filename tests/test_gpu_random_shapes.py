@@ -1,0 +1,106 @@
+"""Seeded random parity sweep over the plan space: format, output dtype, bias, SiLU, alpha, scale
+layout, batch (shared or per-problem bias) and shapes with ragged M, N and K tails, on whichever
+kernel, tile and split count plan creation picks.  Every problem of every call is compared with the
+fp64 oracle (all rows for small problems, sampled rows for large ones), and entries left unwritten
+are caught by poisoning D first.  The cases are fixed by the seed, so a failure names its case."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_gemm_amd as bsg
+import seeded_inputs as si
+from oracle import compare, reference
+
+pytestmark = pytest.mark.gpu
+
+
+def _ktile(s: np.ndarray) -> np.ndarray:
+    """K-tile-major scale layout from its definition: code 4g + c of row r at byte (g * rows + r) * 4
+    + c; padding codes of the last group 0."""
+    rows, kb = s.shape
+    out = np.zeros(-(-kb // 4) * rows * 4, dtype=np.uint8)
+    r = np.arange(rows)
+    for k in range(kb):
+        g, c = divmod(k, 4)
+        out[(g * rows + r) * 4 + c] = s[:, k]
+    return out
+
+
+def _cases(n_small=150, n_large=24, seed=2026):
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_small + n_large):
+        large = i >= n_small
+        fmt = ("mxfp8", "nvfp4")[i % 2]
+        if large:  # enough tiles for the large-shape kernels (K % 512 == 0 half the time), ragged edges
+            M = int(g.integers(2000, 6000))
+            N = 16 * int(g.integers(125, 380))
+            K = 512 * int(g.integers(1, 5)) if g.integers(0, 2) else 32 * int(g.integers(1, 40))
+            batch = 1
+        else:
+            M = int(g.choice([g.integers(1, 65), g.integers(65, 300), g.integers(300, 700)]))
+            N = 16 * int(g.integers(1, 80))
+            K = 32 * int(g.integers(1, 70))
+            batch = int(g.choice([1, 1, 2, 3]))
+        cases.append(dict(i=i, fmt=fmt, M=M, N=N, K=K, batch=batch, out=str(g.choice(["bf16", "f16"])),
+                          bias=bool(g.integers(0, 2)), silu=bool(g.integers(0, 2)),
+                          layout=str(g.choice(["linear", "ktile"])), alpha=float(g.choice([1.0, 0.5, 0.75, 2.0])),
+                          bias_per_problem=bool(g.integers(0, 2))))
+    return cases
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "{i}-{fmt}-{M}x{N}x{K}-b{batch}-{out}-{layout}".format(**c))
+def test_random_plan_parity(case):
+    c = case
+    fmt, M, N, K, L = c["fmt"], c["M"], c["N"], c["K"], c["batch"]
+    print(f"[random] {c}", flush=True)
+    problems = [si.problem(fmt, M, N, K, seed=10000 + 97 * c["i"] + z, alpha=c["alpha"], bias=c["bias"],
+                           silu=c["silu"], out=c["out"]) for z in range(L)]
+    shared_bias = c["bias"] and not c["bias_per_problem"]
+    if shared_bias:
+        for q in problems[1:]:
+            q["bias"] = problems[0]["bias"]
+    # batched: each operand's packed stride rounded up to the alignment plan creation requires (16
+    # bytes for A, B, D; 4 for scales and bias), the gaps filled with 0xFF (NaN in E4M3, E8M0 and the
+    # NVFP4 scale codes), so a kernel that read past a problem's own bytes would fail the comparison
+    up = lambda x, a: -(-x // a) * a  # noqa: E731
+    packed = bsg.packed_strides(fmt, M, N, K, c["layout"])
+    strides = dict(a=up(packed["a"], 16), b=up(packed["b"], 16), sa=up(packed["sa"], 4), sb=up(packed["sb"], 4),
+                   bias=4 * N if c["bias"] and c["bias_per_problem"] else 0, d=up(2 * M * N, 16))
+    plan = bsg.Plan(fmt, M, N, K, out=c["out"], bias=c["bias"], silu=c["silu"], batch=L,
+                    strides=strides if L > 1 else None, scale_layout=c["layout"])
+    info = plan.info()
+    print(f"[random] plan {info['variant']} grid={info['grid']} ws={info['workspace_bytes']}", flush=True)
+    pack = _ktile if c["layout"] == "ktile" else (lambda a: a)
+
+    def cat(key, stride, f=lambda a: a):
+        buf = np.full(L * stride, 0xFF, dtype=np.uint8)
+        for z, q in enumerate(problems):
+            b = np.ascontiguousarray(f(q[key])).reshape(-1).view(np.uint8)
+            buf[z * stride:z * stride + b.size] = b
+        return torch.from_numpy(buf).cuda()
+
+    A, B = cat("A", strides["a"]), cat("B", strides["b"])
+    sA, sB = cat("sA", strides["sa"], pack), cat("sB", strides["sb"], pack)
+    bias = None
+    if c["bias"]:
+        bias = (cat("bias", strides["bias"], lambda a: a.astype(np.float32)) if c["bias_per_problem"] and L > 1
+                else torch.from_numpy(problems[0]["bias"].astype(np.float32)).cuda())
+    D = torch.full((L * strides["d"] // 2,), 0x7FFF, dtype=torch.int16, device="cuda")
+    plan.run(A, B, sA, sB, D, alpha=c["alpha"], bias=bias)
+    torch.cuda.synchronize()
+    Dh = D.cpu().numpy().view(np.uint16)
+    dz = strides["d"] // 2
+    out = [Dh[z * dz:z * dz + M * N].reshape(M, N) for z in range(L)]
+    gaps = [Dh[z * dz + M * N:(z + 1) * dz] for z in range(L)]
+    assert all((g == 0x7FFF).all() for g in gaps), "a store landed between problems"
+    rows = None if M * N <= 600 * 1300 else np.unique(np.concatenate([np.arange(0, M, max(1, M // 20)), [M - 1]]))
+    for z, q in enumerate(problems):
+        got = out[z] if rows is None else out[z][rows]
+        assert not (got == 0x7FFF).any(), f"problem {z}: entries never written"
+        rep = compare(got, reference(q, rows=rows), q["alpha"], q["silu"], q["out"])
+        assert rep["ok"], (z, rep)
+    plan.close()
