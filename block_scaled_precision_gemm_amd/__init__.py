@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_nvfp4_f16",
-           "FORMATS", "OUT_DTYPES", "SCALE_LAYOUTS", "abi_version", "packed_strides", "Problem", "PROBLEM_V1_SIZE",
+           "FORMATS", "OUT_DTYPES", "SCALE_LAYOUTS", "abi_version", "packed_strides", "Problem", "PROBLEM_V1_SIZE", "PROBLEM_V2_SIZE",
            "pack_scales", "scales_ktile_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,10 +45,12 @@ class Problem(ctypes.Structure):
                 ("flags", ctypes.c_uint32), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("device", ctypes.c_int32), ("batch", ctypes.c_int32), ("stride_a", ctypes.c_int64),
                 ("stride_b", ctypes.c_int64), ("stride_sa", ctypes.c_int64), ("stride_sb", ctypes.c_int64),
-                ("stride_bias", ctypes.c_int64), ("stride_d", ctypes.c_int64)]
+                ("stride_bias", ctypes.c_int64), ("stride_d", ctypes.c_int64),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldd", ctypes.c_int64)]
 
 
 PROBLEM_V1_SIZE = 48  # sizeof(bsg_problem) of ABI 1, still accepted by bsg_plan_create
+PROBLEM_V2_SIZE = 96  # ... and of ABI 2 (no leading dimensions)
 
 
 def scales_ktile_bytes(rows: int, codes_per_row: int) -> int:
@@ -56,14 +58,17 @@ def scales_ktile_bytes(rows: int, codes_per_row: int) -> int:
     return 0 if rows < 1 or codes_per_row < 1 else (codes_per_row + 3) // 4 * rows * 4
 
 
-def packed_strides(fmt: str, M: int, N: int, K: int, scale_layout: str = "linear") -> dict:
-    """Byte strides of densely packed batched operands (bias shared by every problem)."""
+def packed_strides(fmt: str, M: int, N: int, K: int, scale_layout: str = "linear", lda: int = 0, ldb: int = 0,
+                   ldd: int = 0) -> dict:
+    """Byte strides of back-to-back batched operands (bias shared by every problem): each problem's
+    A, B and D take rows x leading dimension (0 = packed: K, K, N)."""
     elem, blk = (1.0, 32) if fmt == "mxfp8" else (0.5, 16)
+    lda, ldb, ldd = lda or K, ldb or K, ldd or N
     if scale_layout == "ktile":
         sa, sb = scales_ktile_bytes(M, K // blk), scales_ktile_bytes(N, K // blk)
     else:
         sa, sb = M * K // blk, N * K // blk
-    return dict(a=int(M * K * elem), b=int(N * K * elem), sa=sa, sb=sb, bias=0, d=2 * M * N)
+    return dict(a=int(M * lda * elem), b=int(N * ldb * elem), sa=sa, sb=sb, bias=0, d=2 * M * ldd)
 
 
 class PlanInfo(ctypes.Structure):
@@ -147,13 +152,14 @@ class Plan:
     """A cached GEMM plan: D = epi(alpha * A x B^T (+ bias)) for one problem shape and variant.
 
     batch > 1: that many problems of this shape per call; problem z uses each pointer advanced by
-    strides[key] * z bytes (keys a, b, sa, sb, bias, d; default: packed operands, shared bias).
+    strides[key] * z bytes (keys a, b, sa, sb, bias, d; default: back-to-back operands, shared bias).
     scale_layout "ktile": sA and sB in the K-tile-major layout (pack_scales converts).
+    lda, ldb, ldd: leading dimensions in elements (row pitch of A, B and D; 0 = packed).
     """
 
     def __init__(self, fmt: str, M: int, N: int, K: int, out: str = "bf16", bias: bool = False,
                  silu: bool = False, device: int = -1, batch: int = 1, strides: dict | None = None,
-                 scale_layout: str = "linear"):
+                 scale_layout: str = "linear", lda: int = 0, ldb: int = 0, ldd: int = 0):
         if scale_layout not in SCALE_LAYOUTS:
             raise ValueError(f"scale_layout must be one of {SCALE_LAYOUTS}")
         lib = load_library()
@@ -161,13 +167,14 @@ class Plan:
         self._h = None
         self.fmt, self.M, self.N, self.K, self.out, self.bias, self.silu = fmt, M, N, K, out, bias, silu
         self.batch, self.scale_layout = batch, scale_layout
-        st = packed_strides(fmt, M, N, K, scale_layout)
+        st = packed_strides(fmt, M, N, K, scale_layout, lda, ldb, ldd)
         st.update(strides or {})
         self.strides = st
+        self.lda, self.ldb, self.ldd = lda or K, ldb or K, ldd or N
         prob = Problem(ctypes.sizeof(Problem), FORMATS[fmt], OUT_DTYPES[out],
                        (EPI_BIAS if bias else 0) | (EPI_SILU if silu else 0)
                        | (SCALES_KTILE if scale_layout == "ktile" else 0), M, N, K, device, batch,
-                       st["a"], st["b"], st["sa"], st["sb"], st["bias"], st["d"])
+                       st["a"], st["b"], st["sa"], st["sb"], st["bias"], st["d"], lda, ldb, ldd)
         h = _VP()
         _check(lib.bsg_plan_create(ctypes.byref(prob), ctypes.byref(h)))
         self._h = h

@@ -147,24 +147,32 @@ void device_free(int dev, void* p) {
 
 static_assert(offsetof(bsg_problem, batch) == 44 && offsetof(bsg_problem, stride_a) == BSG_PROBLEM_V1_SIZE,
               "the batch fields extend the ABI-1 layout (batch sits in its tail padding)");
+static_assert(offsetof(bsg_problem, lda) == BSG_PROBLEM_V2_SIZE && sizeof(bsg_problem) == BSG_PROBLEM_V2_SIZE + 24,
+              "the leading dimensions extend the ABI-2 layout");
 
 // Copy the caller's problem into `out`, reading only the bytes its struct_size covers: an ABI-1
-// problem (no batch fields) becomes a single problem.
+// problem (no batch fields) becomes a single problem; ABI-1 and ABI-2 problems are packed (no
+// leading dimensions).
 bsg_status normalize(const bsg_problem* in, bsg_problem* out) {
   memset(out, 0, sizeof(*out));
   if (in->struct_size == sizeof(bsg_problem)) {
     *out = *in;
+  } else if (in->struct_size == BSG_PROBLEM_V2_SIZE) {
+    memcpy(out, in, BSG_PROBLEM_V2_SIZE);
   } else if (in->struct_size == BSG_PROBLEM_V1_SIZE) {
     memcpy(out, in, offsetof(bsg_problem, batch));
-    out->struct_size = sizeof(bsg_problem);
   } else {
-    set_error("bsg_problem.struct_size is %u, expected %zu (or %u for ABI 1)", in->struct_size, sizeof(bsg_problem),
-              BSG_PROBLEM_V1_SIZE);
+    set_error("bsg_problem.struct_size is %u, expected %zu (or %u / %u for ABI 1 / 2)", in->struct_size,
+              sizeof(bsg_problem), BSG_PROBLEM_V1_SIZE, BSG_PROBLEM_V2_SIZE);
     return BSG_ERR_ABI;
   }
+  out->struct_size = sizeof(bsg_problem);
   if (out->batch == 0) out->batch = 1;
   if (out->batch == 1) out->stride_a = out->stride_b = out->stride_sa = out->stride_sb = out->stride_bias =
       out->stride_d = 0;
+  if (out->lda == 0) out->lda = out->K;
+  if (out->ldb == 0) out->ldb = out->K;
+  if (out->ldd == 0) out->ldd = out->N;
   return BSG_OK;
 }
 
@@ -200,9 +208,20 @@ bsg_status validate(const bsg_problem* p) {
     set_error("NVFP4 K %% 32 == 16 is not covered by a compiled kernel (K = %lld)", (long long)p->K);
     return BSG_ERR_UNSUPPORTED;
   }
-  // element offsets must fit the kernels' 32-bit tile arithmetic and the output size size_t math
-  if ((p->M * p->K) >> 31 || (p->N * p->K) >> 31 || (p->M * p->N) >> 31) {
-    set_error("operand or output has >= 2^31 elements; not covered");
+  if (p->lda < p->K || p->ldb < p->K || p->ldd < p->N || p->lda > lim || p->ldb > lim || p->ldd > lim) {
+    set_error("leading dimensions must be in [K, 2^30] for A and B and [N, 2^30] for D (got %lld, %lld, %lld)",
+              (long long)p->lda, (long long)p->ldb, (long long)p->ldd);
+    return BSG_ERR_SHAPE;
+  }
+  const int64_t ld_mult = p->format == BSG_FMT_MXFP8 ? 16 : 32;  // 16-byte rows
+  if (p->lda % ld_mult || p->ldb % ld_mult || p->ldd % 8) {
+    set_error("leading dimensions must keep rows 16-byte aligned: lda, ldb multiples of %lld, ldd of 8",
+              (long long)ld_mult);
+    return BSG_ERR_ALIGN;
+  }
+  // element offsets (rows times pitch) must fit the kernels' 32-bit tile arithmetic
+  if ((p->M * p->lda) >> 31 || (p->N * p->ldb) >> 31 || (p->M * p->ldd) >> 31) {
+    set_error("operand or output spans >= 2^31 elements; not covered");
     return BSG_ERR_UNSUPPORTED;
   }
   if (p->batch < 1 || p->batch > 65535) {
@@ -270,7 +289,8 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   const bool bias = problem->flags & BSG_EPI_BIAS, silu = problem->flags & BSG_EPI_SILU;
   const bsg::Out out = problem->out_dtype == BSG_OUT_F16 ? bsg::Out::F16 : bsg::Out::BF16;
   const bsg::KernelVariant* table = problem->format == BSG_FMT_MXFP8
-                                        ? bsg::mxfp8_variants(problem->M, problem->N, problem->K, problem->batch)
+                                        ? bsg::mxfp8_variants(problem->M, problem->N, problem->K, problem->batch,
+                                                              problem->lda == problem->K && problem->ldb == problem->K)
                                         : bsg::nvfp4_variants(problem->M, problem->N, problem->K, problem->batch);
   if (!table) {
     set_error("no kernel variant covers M=%lld N=%lld K=%lld", (long long)problem->M, (long long)problem->N,
@@ -312,6 +332,10 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   a.stride_sb = problem->stride_sb;
   a.stride_bias = problem->stride_bias;
   a.stride_d = problem->stride_d;
+  const int64_t elem_den = problem->format == BSG_FMT_MXFP8 ? 1 : 2;  // elements per byte
+  a.row_a = (int)(problem->lda / elem_den);
+  a.row_b = (int)(problem->ldb / elem_den);
+  a.ldd = (int)problem->ldd;
   if (a.splits > 1) {
     const size_t bytes =
         (size_t)problem->batch * a.splits * (size_t)problem->M * (size_t)problem->N * sizeof(float);

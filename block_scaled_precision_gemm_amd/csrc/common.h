@@ -34,6 +34,9 @@ struct GemmArgs {
   // Batched problems: grid.z = batch count; batch z uses each pointer advanced by z * its stride
   // (bytes; a stride of 0 shares one matrix / bias vector among all batches).
   int64_t stride_a, stride_b, stride_sa, stride_sb, stride_bias, stride_d;
+  // Row pitches: bytes per row of A and of B, elements per row of D (packed: K or K/2, and N).
+  // Split-K partials stay packed [M][N].
+  int row_a, row_b, ldd;
 };
 
 // Byte offset of scale code `blk` (K block) of operand row `row` in either scale layout: row-major
@@ -75,8 +78,9 @@ struct KernelVariant {
 
 // Variant tables, one per format: index = out dtype (0 bf16, 1 f16) * 4 + bias * 2 + silu.
 // Each kernel family returns its table for the M bucket it serves.
-// `batch`: problems per launch (the grid holds tiles x batch workgroups).
-const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K, int64_t batch);
+// `batch`: problems per launch (the grid holds tiles x batch workgroups).  `packed_ab`: A and B rows
+// are K bytes apart (the large-shape MXFP8 kernel's copies assume it).
+const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K, int64_t batch, bool packed_ab);
 const KernelVariant* mxfp8_tiled_variants(int64_t M, int64_t N, int64_t batch);
 const KernelVariant* mxfp8_pp_variants();
 const KernelVariant* nvfp4_variants(int64_t M, int64_t N, int64_t K, int64_t batch);

@@ -23,12 +23,13 @@
 
 namespace bsg {
 
-// Kernel choice by shape: the 8-wave ping-pong kernel for K % 512 == 0 once 256 x 256 tiles give at
-// least one workgroup per CU; the two-stage tiled kernels (256 x 256 or 128 x 128 tiles, split K for
-// small tile grids, a partial last K tile for K % 128 != 0) for every other K % 32 == 0.
-const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K, int64_t batch) {
+// Kernel choice by shape: the 8-wave ping-pong kernel for K % 512 == 0 with packed A and B rows once
+// 256 x 256 tiles give at least one workgroup per CU; the tiled kernels (256 x 256 or 128 x 128
+// tiles, split K for small tile grids, a partial last K tile for K % 128 != 0, any row pitch) for
+// every other K % 32 == 0.
+const KernelVariant* mxfp8_variants(int64_t M, int64_t N, int64_t K, int64_t batch, bool packed_ab) {
   const int64_t large_tiles = ((M + 255) / 256) * ((N + 255) / 256) * batch;
-  if (K % 512 == 0 && large_tiles >= 256) return mxfp8_pp_variants();
+  if (packed_ab && K % 512 == 0 && large_tiles >= 256) return mxfp8_pp_variants();
   return mxfp8_tiled_variants(M, N, batch);
 }
 

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
     const int row = 8 * q + (lane >> 3);
     const v4i v = *(const v4i*)(eb + row * EPI_ROW + 2 * cc);
     const int m = mw + row, n = nw + cc;
-    if (m < p.M && n < p.N) *(v4i*)(D + (size_t)m * p.N + n) = v;
+    if (m < p.M && n < p.N) *(v4i*)(D + (size_t)m * p.ldd + n) = v;
   }
 }
 

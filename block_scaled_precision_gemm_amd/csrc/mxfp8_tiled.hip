@@ -166,13 +166,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
 
   // operand buffers start at the tile's first row and end at the last valid row
   const __amdgpu_buffer_rsrc_t rsA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (size_t)m0 * K), (short)0, m_valid * K, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (size_t)m0 * p.row_a), (short)0, (m_valid - 1) * p.row_a + K,
+                                        kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rsB =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (size_t)n0 * K), (short)0, n_valid * K, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (size_t)n0 * p.row_b), (short)0, (n_valid - 1) * p.row_b + K,
+                                        kRsrcWord3);
   CopyPlan<C::A_COPIES> cpA;
   CopyPlan<C::B_COPIES> cpB;
-  cpA.init(wave, lane, K);
-  cpB.init(wave, lane, K);
+  cpA.init(wave, lane, p.row_a);
+  cpB.init(wave, lane, p.row_b);
 
   // per-lane LDS offsets of the two 16-byte chunks of k-step ks (see the layout comment above)
   const int f = swz(r);
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
       const v4i v = *(const v4i*)(eb + row * EROW + 16 * pc);
       const int m = mw + 32 * i + row, n = nw + pc * (16 / ES);
       if (m < p.M && n < p.N) {
-        v4i* const dst = (v4i*)(out + ((size_t)m * p.N + n) * ES);
+        v4i* const dst = (v4i*)(out + ((size_t)m * (SPLIT ? p.N : p.ldd) + n) * ES);
         if constexpr (SPLIT)
           __builtin_nontemporal_store(v, dst);  // partials: streaming store, read once by the finish kernel
         else

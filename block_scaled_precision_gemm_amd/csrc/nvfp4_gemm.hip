@@ -145,7 +145,9 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 
   // Buffer resources of the shared and private operand rows of this tile (rows past M / N fall
   // outside the range and read as zeros).
-  const uint8_t* s_q = SHARED_A ? p.A + (size_t)m0 * KH : p.B + (size_t)n0 * KH;
+  // row pitches (bytes) of the shared and private operands
+  const uint32_t s_pitch = (uint32_t)(SHARED_A ? p.row_a : p.row_b), p_pitch = (uint32_t)(SHARED_A ? p.row_b : p.row_a);
+  const uint8_t* s_q = SHARED_A ? p.A + (size_t)m0 * s_pitch : p.B + (size_t)n0 * s_pitch;
   // Scale codes: row-major [rows][KS], or K-tile-major (the 4 codes of K tile kt of row r at
   // (kt * rows + r) * 4): per-lane offsets from the tile's first row plus kt * (4 or 4 * rows).
   const bool ktile = p.scale_ktile != 0;
@@ -154,19 +156,19 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   const uint32_t s_rowb = ktile ? 4u : KS, s_ktb = ktile ? 4u * (uint32_t)s_all : 4u;
   const uint32_t p_rowb = ktile ? 4u : KS, p_ktb = ktile ? 4u * (uint32_t)p_all : 4u;
   const uint8_t* s_s = (SHARED_A ? p.sA : p.sB) + (size_t)s_first * s_rowb;
-  const uint8_t* p_q = SHARED_A ? p.B + (size_t)n0 * KH : p.A + (size_t)m0 * KH;
+  const uint8_t* p_q = SHARED_A ? p.B + (size_t)n0 * p_pitch : p.A + (size_t)m0 * p_pitch;
   const uint8_t* p_s = (SHARED_A ? p.sB : p.sA) + (size_t)p_first * p_rowb;
   const int s_rows = SHARED_A ? min(BS, p.M - m0) : min(BS, p.N - n0);
   const int p_rows = SHARED_A ? min(BP, p.N - n0) : min(BP, p.M - m0);
   const __amdgpu_buffer_rsrc_t rs_q =
-      __builtin_amdgcn_make_buffer_rsrc((void*)s_q, (short)0, (int)(s_rows * KH), (int)kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)s_q, (short)0, (int)((s_rows - 1) * s_pitch + KH), (int)kRsrcWord3);
   // (K-tile-major: the range ends at the array's end; rows past the operand's last row read other
   // rows' codes, which only reach outputs that are never stored)
   const uint32_t groups = (KS + 3) >> 2;
   const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
       (void*)s_s, (short)0, (int)(ktile ? groups * 4u * (uint32_t)s_all - 4u * (uint32_t)s_first : s_rows * KS), (int)kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rp_q =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p_q, (short)0, (int)(p_rows * KH), (int)kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)p_q, (short)0, (int)((p_rows - 1) * p_pitch + KH), (int)kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rp_s = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p_s, (short)0, (int)(ktile ? groups * 4u * (uint32_t)p_all - 4u * (uint32_t)p_first : p_rows * KS), (int)kRsrcWord3);
 
@@ -188,7 +190,8 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     const int R = 32 * q + (lane >> 1);
     const int row = q < NSC ? R : R - BS;  // row within its operand's tile rows
     half = data ? (lane & 1) ^ ((R >> 3) & 1) : (lane & 1);
-    off = data ? (uint32_t)row * KH + 16u * half : (uint32_t)row * (q < NSC ? s_rowb : p_rowb) + 2u * half;
+    off = data ? (uint32_t)row * (q < NSC ? s_pitch : p_pitch) + 16u * half
+               : (uint32_t)row * (q < NSC ? s_rowb : p_rowb) + 2u * half;
   };
   uint32_t o_pd, o_ps, o_sd, o_ss;
   int h_unused;
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
         uint2 o;
         o.x = pack2_out<O>(epi_value<SILU>(v[0], alpha, b[0]), epi_value<SILU>(v[1], alpha, b[1]));
         o.y = pack2_out<O>(epi_value<SILU>(v[2], alpha, b[2]), epi_value<SILU>(v[3], alpha, b[3]));
-        *(uint2*)((uint16_t*)p.D + (size_t)m * p.N + n) = o;
+        *(uint2*)((uint16_t*)p.D + (size_t)m * p.ldd + n) = o;
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass overwrites

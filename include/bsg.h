@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define BSG_ABI_VERSION 2
+#define BSG_ABI_VERSION 3
 
 typedef enum bsg_status {
   BSG_OK = 0,
@@ -100,7 +100,7 @@ enum {
 };
 
 typedef struct bsg_problem {
-  uint32_t struct_size; /* = sizeof(bsg_problem), or BSG_PROBLEM_V1_SIZE (then batch = 1); else BSG_ERR_ABI */
+  uint32_t struct_size; /* = sizeof(bsg_problem), or the ABI-1 / ABI-2 size below; else BSG_ERR_ABI */
   int32_t format;       /* bsg_format */
   int32_t out_dtype;    /* bsg_out_dtype */
   uint32_t flags;       /* BSG_EPI_*, BSG_SCALES_KTILE */
@@ -114,10 +114,20 @@ typedef struct bsg_problem {
    * (not checked).  batch 0 is read as 1; strides are ignored when batch is 1. */
   int32_t batch;
   int64_t stride_a, stride_b, stride_sa, stride_sb, stride_bias, stride_d;
+  /* Leading dimensions (ABI 3), in elements; 0 = packed (lda = ldb = K, ldd = N).  Row m of A starts
+   * lda elements after row m - 1 (NVFP4: lda / 2 bytes), row n of B ldb elements after row n - 1,
+   * row m of D ldd elements after row m - 1; the gaps are never read or written.  Each must be at
+   * least its packed value and keep every row 16-byte aligned: lda, ldb multiples of 16 (MXFP8) or
+   * 32 (NVFP4), ldd a multiple of 8.  Scales stay packed, in either scale layout.  Leading
+   * dimensions apply to every problem of a batch (batch strides are separate).  Strided A or B is
+   * served by the tiled kernels (the large-shape MXFP8 kernel takes packed A and B). */
+  int64_t lda, ldb, ldd;
 } bsg_problem;
 
-/* sizeof(bsg_problem) of ABI 1 (no batch fields): still accepted, as a single problem. */
+/* sizeof(bsg_problem) of ABI 1 (no batch or leading-dimension fields) and of ABI 2 (no leading-
+ * dimension fields): still accepted, with the missing fields read as 0. */
 #define BSG_PROBLEM_V1_SIZE 48u
+#define BSG_PROBLEM_V2_SIZE 96u
 
 typedef struct bsg_plan_s* bsg_plan; /* opaque, library-owned */
 

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = bsg.load_library()
-    assert lib.bsg_abi_version() == 2
+    assert lib.bsg_abi_version() == 3
     for code, name in bsg.STATUS.items():
         assert lib.bsg_status_string(code).decode() == name
 
@@ -66,6 +66,18 @@ def test_batched_plan_validation(fields, status):
     assert not h.value
 
 
+@pytest.mark.parametrize("fields,status", [
+    (dict(lda=128), 2), (dict(ldb=240), 2), (dict(ldd=128), 2),         # below the packed value
+    (dict(lda=264), 4), (dict(ldb=280), 4), (dict(ldd=260), 4),         # rows not 16-byte aligned
+    (dict(format=2, lda=272), 4),                                       # NVFP4: 136 bytes per row
+    (dict(lda=1 << 31), 2), (dict(M=1 << 16, lda=1 << 15), 3),          # too large, spans >= 2^31
+])
+def test_leading_dimension_validation(fields, status):
+    st, h = _create(**fields)
+    assert st == status, bsg.load_library().bsg_last_error()
+    assert not h.value
+
+
 def test_abi1_problem_size_is_accepted():
     """An ABI-1 caller (48-byte bsg_problem, no batch fields) still passes validation: without a GPU
     it reaches the device check; any other size is an ABI error."""
@@ -76,6 +88,11 @@ def test_abi1_problem_size_is_accepted():
     assert st == 5, bsg.load_library().bsg_last_error()
     st, _ = _create(struct_size=bsg.PROBLEM_V1_SIZE + 8)
     assert st == 8
+    # ABI 2 (96 bytes, no leading dimensions): the fields past it are not read (here invalid ones)
+    st, _ = _create(struct_size=bsg.PROBLEM_V2_SIZE, lda=8, ldb=8, ldd=8)
+    assert st == 5, bsg.load_library().bsg_last_error()
+    st, _ = _create(lda=512, ldb=288, ldd=272)  # valid leading dimensions reach the device check
+    assert st == 5, bsg.load_library().bsg_last_error()
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -87,15 +104,16 @@ def test_struct_layout_matches_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stddef.h>\n#include <stdio.h>\n#include "bsg.h"\n'
-        "int main(void) { printf(\"%zu %zu %zu %zu %zu %zu %u\\n\", sizeof(bsg_problem), offsetof(bsg_problem, device),"
-        " offsetof(bsg_problem, batch), offsetof(bsg_problem, stride_a), offsetof(bsg_problem, stride_d),"
-        " sizeof(bsg_plan_info), BSG_PROBLEM_V1_SIZE); return 0; }\n")
+        "int main(void) { printf(\"%zu %zu %zu %zu %zu %zu %u %zu %zu %u\\n\", sizeof(bsg_problem),"
+        " offsetof(bsg_problem, device), offsetof(bsg_problem, batch), offsetof(bsg_problem, stride_a),"
+        " offsetof(bsg_problem, stride_d), sizeof(bsg_plan_info), BSG_PROBLEM_V1_SIZE,"
+        " offsetof(bsg_problem, lda), offsetof(bsg_problem, ldd), BSG_PROBLEM_V2_SIZE); return 0; }\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     P = bsg.Problem
     want = [ctypes.sizeof(P), P.device.offset, P.batch.offset, P.stride_a.offset, P.stride_d.offset,
-            ctypes.sizeof(bsg.PlanInfo), bsg.PROBLEM_V1_SIZE]
+            ctypes.sizeof(bsg.PlanInfo), bsg.PROBLEM_V1_SIZE, P.lda.offset, P.ldd.offset, bsg.PROBLEM_V2_SIZE]
     assert got == want
 
 

@@ -1,5 +1,6 @@
 """Seeded random parity sweep over the plan space: format, output dtype, bias, SiLU, alpha, scale
-layout, batch (shared or per-problem bias) and shapes with ragged M, N and K tails, on whichever
+layout, batch (shared or per-problem bias), leading dimensions (row gaps filled with codes that would
+change the result if read) and shapes with ragged M, N and K tails, on whichever
 kernel, tile and split count plan creation picks.  Every problem of every call is compared with the
 fp64 oracle (all rows for small problems, sampled rows for large ones), and entries left unwritten
 are caught by poisoning D first.  The cases are fixed by the seed, so a failure names its case."""
@@ -46,13 +47,19 @@ def _cases(n_small=150, n_large=24, seed=2026):
                           bias=bool(g.integers(0, 2)), silu=bool(g.integers(0, 2)),
                           layout=str(g.choice(["linear", "ktile"])), alpha=float(g.choice([1.0, 0.5, 0.75, 2.0])),
                           bias_per_problem=bool(g.integers(0, 2))))
+        mult = 16 if fmt == "mxfp8" else 32  # elements per 16 bytes
+        c = cases[-1]
+        c["lda"] = K + mult * int(g.integers(1, 5)) if g.integers(0, 3) == 0 else K
+        c["ldb"] = K + mult * int(g.integers(1, 5)) if g.integers(0, 3) == 0 else K
+        c["ldd"] = N + 8 * int(g.integers(1, 5)) if g.integers(0, 3) == 0 else N
     return cases
 
 
 CASES = _cases()
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "{i}-{fmt}-{M}x{N}x{K}-b{batch}-{out}-{layout}".format(**c))
+@pytest.mark.parametrize("case", CASES,
+                         ids=lambda c: "{i}-{fmt}-{M}x{N}x{K}-b{batch}-{out}-{layout}-ld{lda}.{ldb}.{ldd}".format(**c))
 def test_random_plan_parity(case):
     c = case
     fmt, M, N, K, L = c["fmt"], c["M"], c["N"], c["K"], c["batch"]
@@ -67,11 +74,13 @@ def test_random_plan_parity(case):
     # bytes for A, B, D; 4 for scales and bias), the gaps filled with 0xFF (NaN in E4M3, E8M0 and the
     # NVFP4 scale codes), so a kernel that read past a problem's own bytes would fail the comparison
     up = lambda x, a: -(-x // a) * a  # noqa: E731
-    packed = bsg.packed_strides(fmt, M, N, K, c["layout"])
+    lda, ldb, ldd = c["lda"], c["ldb"], c["ldd"]
+    epb = 1 if fmt == "mxfp8" else 2  # elements per byte
+    packed = bsg.packed_strides(fmt, M, N, K, c["layout"], lda, ldb, ldd)
     strides = dict(a=up(packed["a"], 16), b=up(packed["b"], 16), sa=up(packed["sa"], 4), sb=up(packed["sb"], 4),
-                   bias=4 * N if c["bias"] and c["bias_per_problem"] else 0, d=up(2 * M * N, 16))
+                   bias=4 * N if c["bias"] and c["bias_per_problem"] else 0, d=up(2 * M * ldd, 16))
     plan = bsg.Plan(fmt, M, N, K, out=c["out"], bias=c["bias"], silu=c["silu"], batch=L,
-                    strides=strides if L > 1 else None, scale_layout=c["layout"])
+                    strides=strides if L > 1 else None, scale_layout=c["layout"], lda=lda, ldb=ldb, ldd=ldd)
     info = plan.info()
     print(f"[random] plan {info['variant']} grid={info['grid']} ws={info['workspace_bytes']}", flush=True)
     pack = _ktile if c["layout"] == "ktile" else (lambda a: a)
@@ -83,7 +92,14 @@ def test_random_plan_parity(case):
             buf[z * stride:z * stride + b.size] = b
         return torch.from_numpy(buf).cuda()
 
-    A, B = cat("A", strides["a"]), cat("B", strides["b"])
+    def pitched(pitch):  # rows `pitch` bytes apart, the row gap 0xFF (E4M3 NaN; E2M1 pairs of -6)
+        def f(x):
+            out = np.full((x.shape[0], pitch), 0xFF, dtype=np.uint8)
+            out[:, :x.shape[1]] = x
+            return out
+        return f
+
+    A, B = cat("A", strides["a"], pitched(lda // epb)), cat("B", strides["b"], pitched(ldb // epb))
     sA, sB = cat("sA", strides["sa"], pack), cat("sB", strides["sb"], pack)
     bias = None
     if c["bias"]:
@@ -94,9 +110,10 @@ def test_random_plan_parity(case):
     torch.cuda.synchronize()
     Dh = D.cpu().numpy().view(np.uint16)
     dz = strides["d"] // 2
-    out = [Dh[z * dz:z * dz + M * N].reshape(M, N) for z in range(L)]
-    gaps = [Dh[z * dz + M * N:(z + 1) * dz] for z in range(L)]
-    assert all((g == 0x7FFF).all() for g in gaps), "a store landed between problems"
+    full = [Dh[z * dz:z * dz + M * ldd].reshape(M, ldd) for z in range(L)]
+    out = [np.ascontiguousarray(f[:, :N]) for f in full]
+    gaps = [Dh[z * dz + M * ldd:(z + 1) * dz] for z in range(L)] + [f[:, N:] for f in full]
+    assert all((g == 0x7FFF).all() for g in gaps), "a store landed outside a problem's rows"
     rows = None if M * N <= 600 * 1300 else np.unique(np.concatenate([np.arange(0, M, max(1, M // 20)), [M - 1]]))
     for z, q in enumerate(problems):
         got = out[z] if rows is None else out[z][rows]
