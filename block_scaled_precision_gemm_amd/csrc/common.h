@@ -27,6 +27,9 @@ struct GemmArgs {
   void* D;                // [M][N] bf16/fp16
   float alpha;
   int M, N, K;
+  // Row pitches: bytes per row of A and of B, elements per row of D (packed: K or K/2, and N).
+  // Split-K partials stay packed [M][N].  (Next to the shape: read in the same kernel-argument load.)
+  int row_a, row_b, ldd;
   int tiles_m, tiles_n;   // output tile grid
   int splits;             // split-K factor (1: none)
   int scale_ktile;        // 0: sA / sB row-major [rows][KB]; 1: K-tile-major [ceil(KB/4)][rows][4]
@@ -34,9 +37,6 @@ struct GemmArgs {
   // Batched problems: grid.z = batch count; batch z uses each pointer advanced by z * its stride
   // (bytes; a stride of 0 shares one matrix / bias vector among all batches).
   int64_t stride_a, stride_b, stride_sa, stride_sb, stride_bias, stride_d;
-  // Row pitches: bytes per row of A and of B, elements per row of D (packed: K or K/2, and N).
-  // Split-K partials stay packed [M][N].
-  int row_a, row_b, ldd;
 };
 
 // Byte offset of scale code `blk` (K block) of operand row `row` in either scale layout: row-major
