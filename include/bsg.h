@@ -31,6 +31,8 @@
  * contiguous; codes past KB in the last group are padding (never used).  Size
  * G * rows * 4 bytes per operand; bsg_pack_scales converts.
  * bias: float[N] (fp32), broadcast over rows.  D: bf16/fp16 [M][N] row-major.
+ * Shapes above are the packed case; with leading dimensions (bsg_problem.lda / ldb / ldd) the rows
+ * of A, B and D sit lda, ldb and ldd elements apart instead.
  * All operand pointers are device pointers.
  *
  * Life cycle (the per-call work that the issue #3003 page measures as 534 of
