@@ -114,12 +114,16 @@ __device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
   return make_int2(first_m + in_group % gsize, in_group / gsize);
 }
 
-template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT>
+// SC4: scale codes copied 4 bytes per row and K tile (one copy per wave covers 64 rows), for scale
+// rows that are dword-aligned (K-tile-major layout, or row-major with K % 64 == 0); otherwise 2 bytes
+// per row half (two copies per wave).
+template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT, bool SC4>
 __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   select_batch(p);
   constexpr int BS = CF::BS, BP = CF::BP, TS = CF::TS, TP = CF::TP, NSC = CF::NSC;
   constexpr int RAW_DATA = CF::RAW_DATA, RAW_STAGE = CF::RAW_STAGE, DEC_STAGE = CF::DEC_STAGE;
   constexpr int BM = SHARED_A ? BS : BP, BN = SHARED_A ? BP : BS;
+  constexpr int NCOP = SC4 ? COPIES - 1 : COPIES;  // copies per wave per K tile
   __shared__ __attribute__((aligned(16))) uint8_t lds[CF::LDS_BYTES];
   uint8_t* const raw = lds;
   uint8_t* const dec = lds + NR * RAW_STAGE;
@@ -199,6 +203,15 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   copy_off(qp, false, o_ps, h_unused);
   copy_off(qs, true, o_sd, h_unused);
   copy_off(qs, false, o_ss, h_unused);
+  // SC4: wave w copies the codes of stage rows 64 c4 .. 64 c4 + 63 (4 bytes each) into RAW_DATA +
+  // 256 c4; with 384 rows (BS = 128) waves 6 and 7 repeat copies 4 and 5 (same bytes, same place).
+  constexpr int SC4_COPIES = CF::ROWS / 64;
+  static_assert(SC4_COPIES <= 8 && 2 * SC4_COPIES >= 8 && BS % 64 == 0, "one 64-row scale copy per wave");
+  const int c4 = wave < SC4_COPIES ? wave : wave - (8 - SC4_COPIES);
+  const bool c4_shared = 64 * c4 < BS;  // wave-uniform
+  const uint32_t o_s4 = (uint32_t)(64 * c4 + lane - (c4_shared ? 0 : BS)) * (c4_shared ? s_rowb : p_rowb);
+  const __amdgpu_buffer_rsrc_t r4_s = c4_shared ? rs_s : rp_s;
+  const uint32_t ktb4 = c4_shared ? s_ktb : p_ktb;
   const __amdgpu_buffer_rsrc_t r2_q = has_shared ? rs_q : rp_q;
   const __amdgpu_buffer_rsrc_t r2_s = has_shared ? rs_s : rp_s;
   const uint32_t ktb2 = has_shared ? s_ktb : p_ktb;
@@ -213,9 +226,13 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     kt = min(kt, ke - 1);  // past the last tile re-read it (never consumed): uniform load counts
     uint8_t* st = raw + ring(kt) * RAW_STAGE;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_q, (lds_void*)(st + 1024 * qs), 16, o_sd, (uint32_t)kt * 32u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_s, (lds_void*)(st + RAW_DATA + 256 * qs), 2, o_ss, (uint32_t)kt * ktb2, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_q, (lds_void*)(st + 1024 * qp), 16, o_pd, (uint32_t)kt * 32u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_s, (lds_void*)(st + RAW_DATA + 256 * qp), 2, o_ps, (uint32_t)kt * p_ktb, 0, 0);
+    if constexpr (SC4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r4_s, (lds_void*)(st + RAW_DATA + 256 * c4), 4, o_s4, (uint32_t)kt * ktb4, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_s, (lds_void*)(st + RAW_DATA + 256 * qs), 2, o_ss, (uint32_t)kt * ktb2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_s, (lds_void*)(st + RAW_DATA + 256 * qp), 2, o_ps, (uint32_t)kt * p_ktb, 0, 0);
+    }
   };
   // Scale codes of half h of K tile kt, or 0 when that half lies past K.
   // CHECK: the tile may be the split's last one (prologue and drain loops); the steady-state loop
@@ -234,7 +251,13 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   const int sd_row = BS == 256 ? tid >> 1 : tid >> 2;
   const int sd_h = BS == 256 ? tid & 1 : (tid >> 1) & 1, sd_sub = BS == 256 ? 0 : tid & 1;
   const uint32_t sd_raw = (uint32_t)(32 * sd_row + 16 * (sd_h ^ ((sd_row >> 3) & 1)));
-  const uint32_t sd_scale = (uint32_t)(RAW_DATA + 8 * sd_row + 4 * sd_h);
+  // the two codes of row R, half h: a zero-extended 4-byte slot at 8R + 4h, or (SC4) bytes 2h, 2h+1
+  // of the row's 4-byte slot at 4R, read as 2 bytes: the same value either way
+  const uint32_t sd_scale = (uint32_t)(RAW_DATA + (SC4 ? 4 * sd_row + 2 * sd_h : 8 * sd_row + 4 * sd_h));
+  auto scale_pair = [&](const uint8_t* at) -> uint32_t {
+    if constexpr (SC4) return (uint32_t)*(const uint16_t*)at;
+    return *(const uint32_t*)at;
+  };
   uint32_t sd_out[SD_PIECES];
 #pragma unroll
   for (int d = 0; d < SD_PIECES; ++d)
@@ -243,7 +266,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     const uint8_t* st = raw + ring(kt) * RAW_STAGE;
     uint8_t* out = dec + (ring(kt) & 1) * DEC_STAGE;
     const v4i q4 = *(const v4i*)(st + sd_raw);  // the row's half
-    const uint32_t codes = half_scales(*(const uint32_t*)(st + sd_scale), kt, sd_h, check);
+    const uint32_t codes = half_scales(scale_pair(st + sd_scale), kt, sd_h, check);
     if constexpr (BS == 256) {
       v4i r[4];
       e2m1x32_scaled_f16(q4, codes, r);
@@ -265,7 +288,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   for (int j = 0; j < TP; ++j) {
     const int R = BS + 64 * wp + 32 * j + r32;
     pf_raw[j] = (uint32_t)(32 * R + 16 * (hl ^ ((R >> 3) & 1)));
-    pf_scale[j] = (uint32_t)(RAW_DATA + 8 * R + 4 * hl);
+    pf_scale[j] = (uint32_t)(RAW_DATA + (SC4 ? 4 * R + 2 * hl : 8 * R + 4 * hl));
   }
   // Shared block i, slice s: decoded row BS/2 wsh + 32i + r, piece 4 hl + s.
   const uint32_t sf_row = (uint32_t)(128 * (BS / 2 * wsh + r32));
@@ -290,7 +313,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TP; ++j) {
       pq[j] = *(const v4i*)(st + pf_raw[j]);
-      const uint32_t s = e4m3x2_scale_f16x2(half_scales(*(const uint32_t*)(st + pf_scale[j]), kt, hl, check));
+      const uint32_t s = e4m3x2_scale_f16x2(half_scales(scale_pair(st + pf_scale[j]), kt, hl, check));
       ps[j][0] = f16x2_splat_lo(s);
       ps[j][1] = f16x2_splat_hi(s);
     }
@@ -322,10 +345,10 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // Prologue: copies of tiles kb .. kb+DIST-1 (clamped); tile kb's shared rows decoded.
 #pragma unroll
   for (int i = 0; i < DIST; ++i) copy_tile(kb + i);
-  wait_copies<(DIST - 1) * COPIES>();
+  wait_copies<(DIST - 1) * NCOP>();
   lds_barrier();  // every wave's copies of tile kb have landed
   decode_shared(kb, Checked{});
-  wait_copies<(DIST - 2) * COPIES>();
+  wait_copies<(DIST - 2) * NCOP>();
   lds_barrier();  // tile kb decoded, tile kb+1 landed
   // Steady state: step kt issues tile kt+DIST's copies, computes tile kt and decodes tile kt+1's
   // shared rows; before the barrier that ends it, the wave's copies of tile kt+2 must have landed
@@ -337,7 +360,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     for (int c = 0; c < NR; ++c) {
       copy_tile(kt + c + DIST);
       step(kt + c, Unchecked{});
-      wait_copies<(DIST - 2) * COPIES>();
+      wait_copies<(DIST - 2) * NCOP>();
       lds_barrier();
     }
   }
@@ -345,7 +368,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   for (; kt + DIST < ke; ++kt) {
     copy_tile(kt + DIST);
     step(kt, Unchecked{});
-    wait_copies<(DIST - 2) * COPIES>();
+    wait_copies<(DIST - 2) * NCOP>();
     lds_barrier();
   }
   // Last DIST tiles: nothing left to copy.  Leaves no copy in flight past the end of the kernel.
@@ -409,11 +432,14 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU>
 hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
+  const bool sc4 = args.scale_ktile || args.K % 64 == 0;  // scale rows dword-aligned
   if (args.splits <= 1)
-    return hipLaunchKernel((const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, false>, grid, block, kargs, 0,
-                           stream);
-  hipError_t e =
-      hipLaunchKernel((const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, true>, grid, block, kargs, 0, stream);
+    return hipLaunchKernel(sc4 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, false, true>
+                               : (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, false, false>,
+                           grid, block, kargs, 0, stream);
+  hipError_t e = hipLaunchKernel(sc4 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, true, true>
+                                     : (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, true, false>,
+                                 grid, block, kargs, 0, stream);
   if (e != hipSuccess) return e;
   return launch_splitk_finish<O, BIAS, SILU, 16>(args, grid.z, stream);  // accumulators carry 2^-16
 }
