@@ -454,9 +454,9 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
         BSG_NVR(CF, SA, NAME, Out::F16, false, false, MAXS), BSG_NVR(CF, SA, NAME, Out::F16, false, true, MAXS),    \
         BSG_NVR(CF, SA, NAME, Out::F16, true, false, MAXS), BSG_NVR(CF, SA, NAME, Out::F16, true, true, MAXS),      \
   }
-// Split-K cost model (see choose_splits): fitted to split sweeps of small-M shapes (M 64..512,
-// N 1024..8192, K 2048..8192) on MI355X.
-constexpr float kSplitKtileUs = 0.66f, kSplitPartialUsPerMib = 0.34f;
+// Split-K cost model (see choose_splits): fitted to split sweeps of small-M shapes (M 128..256,
+// N 4096..8192, K 4096..8192) on MI355X with streaming partial stores and 4-byte scale copies.
+constexpr float kSplitKtileUs = 0.54f, kSplitPartialUsPerMib = 0.22f;
 constexpr int kMaxSplits = 16;
 static_assert(kMaxSplits <= kMaxFinishSplits, "the finish kernel sums at most kMaxFinishSplits partials");
 const KernelVariant kSharedA[8] = BSG_NVR_TABLE(Cfg128, true, "nvfp4_128x256_sharedA", kMaxSplits);
