@@ -92,13 +92,10 @@ bsg_status check_device(int dev) {
   return BSG_OK;
 }
 
-// Fixed cost of splitting K (microseconds): the finish kernel's launch and ramp.
-constexpr double kFinishUs = 2.4;
-
 // Split-K factor for a kernel that supports it.  Candidates run from 1 to the largest factor that
 // keeps the grid within one workgroup per compute unit (ceil(cus / tiles)), at least 4 K tiles per
 // split and the kernel's maximum; the choice minimises the kernel's cost model
-//   ktile_us * ceil(k_tiles / S) + (S > 1 ? kFinishUs + partial_us_per_mib * S * plane_mib : 0),
+//   ktile_us * ceil(k_tiles / S) + (S > 1 ? split_fixed_us + partial_us_per_mib * S * plane_mib : 0),
 // plane_mib = the fp32 partials of one split (batch x M x N x 4 bytes) in MiB.  A shorter loop per
 // workgroup pays for itself only while it outweighs the partial traffic and the second launch.
 int choose_splits(const bsg::KernelVariant& v, int64_t tiles, int64_t K, double plane_bytes, int cus) {
@@ -111,7 +108,7 @@ int choose_splits(const bsg::KernelVariant& v, int64_t tiles, int64_t K, double 
   int best = 1;
   double best_us = v.ktile_us * (double)k_tiles;
   for (int64_t s = 2; s <= s_max; ++s) {
-    const double us = v.ktile_us * (double)((k_tiles + s - 1) / s) + kFinishUs +
+    const double us = v.ktile_us * (double)((k_tiles + s - 1) / s) + v.split_fixed_us +
                       v.partial_us_per_mib * (double)s * plane_mib;
     if (us < best_us) best_us = us, best = (int)s;
   }

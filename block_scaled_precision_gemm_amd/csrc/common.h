@@ -71,9 +71,10 @@ struct KernelVariant {
   bool linear_grid;      // grid = (tiles_m * tiles_n * splits) workgroups in x; else (tiles_n, tiles_m)
   int max_splits = 1;    // > 1: the kernel supports split-K up to this factor (needs a workspace)
   // Split-K cost model of a split-capable kernel (microseconds, fitted to timings on MI355X): one K
-  // tile of a workgroup's loop while the grid fills at most one workgroup per CU, and one MiB of fp32
-  // partials per split (stored by the GEMM kernel, read back by the finish kernel).
-  float ktile_us = 0.0f, partial_us_per_mib = 0.0f;
+  // tile of a workgroup's loop while the grid fills at most one workgroup per CU, one MiB of fp32
+  // partials per split (stored by the GEMM kernel, read back by the finish kernel), and the fixed
+  // cost of splitting at all (the finish kernel's launch and ramp, the split kernel's own prologue).
+  float ktile_us = 0.0f, partial_us_per_mib = 0.0f, split_fixed_us = 0.0f;
 };
 
 // Variant tables, one per format: index = out dtype (0 bf16, 1 f16) * 4 + bias * 2 + silu.

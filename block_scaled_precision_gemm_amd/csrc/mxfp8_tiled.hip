@@ -480,7 +480,7 @@ hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t
 
 #define BSG_MX_TILED(NAME, C, O, B, S) \
   { NAME, &launch_tiled<C, O, B, S>, C::BM, C::BN, BK, C::THREADS, C::NS * C::STAGE, true, C::MAX_SPLITS, \
-    kSplitKtileUs, kSplitPartialUsPerMib }
+    kSplitKtileUs, kSplitPartialUsPerMib, kSplitFixedUs }
 #define BSG_MX_TABLE(NAME, C)                                                                    \
   {                                                                                              \
     BSG_MX_TILED(NAME, C, Out::BF16, false, false), BSG_MX_TILED(NAME, C, Out::BF16, false, true), \
@@ -522,8 +522,9 @@ BSG_MX_INST(Small3, true, kScaleTile)
 #undef BSG_MX_INST
 
 // Split-K cost model of the 128 x 128 kernel (see choose_splits): fitted to split sweeps of shapes
-// with 16 to 64 tiles and 8 to 64 K tiles on MI355X.  The 256 x 256 configuration never splits.
-constexpr float kSplitKtileUs = 0.60f, kSplitPartialUsPerMib = 0.49f;
+// with 16 to 64 tiles and 8 to 64 K tiles on MI355X (the fixed cost from the unsplit timings of the
+// same shapes).  The 256 x 256 configuration never splits.
+constexpr float kSplitKtileUs = 0.645f, kSplitPartialUsPerMib = 0.31f, kSplitFixedUs = 4.5f;
 static_assert(Small::MAX_SPLITS <= kMaxFinishSplits && Small3::MAX_SPLITS == Small::MAX_SPLITS,
               "the finish kernel sums at most kMaxFinishSplits partials");
 const KernelVariant kLarge[8] = BSG_MX_TABLE("mxfp8_tiled_256x256x128_w8", Large);

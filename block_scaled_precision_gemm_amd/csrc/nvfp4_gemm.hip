@@ -446,7 +446,7 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
 
 #define BSG_NVR(CF, SA, NAME, O, B, S, MAXS)                                                          \
   { NAME, &launch<CF, SA, O, B, S>, SA ? CF::BS : CF::BP, SA ? CF::BP : CF::BS, BK, THREADS, (uint32_t)CF::LDS_BYTES, \
-    true, MAXS, kSplitKtileUs, kSplitPartialUsPerMib }
+    true, MAXS, kSplitKtileUs, kSplitPartialUsPerMib, kSplitFixedUs }
 #define BSG_NVR_TABLE(CF, SA, NAME, MAXS)                                                                          \
   {                                                                                                                 \
     BSG_NVR(CF, SA, NAME, Out::BF16, false, false, MAXS), BSG_NVR(CF, SA, NAME, Out::BF16, false, true, MAXS),      \
@@ -456,7 +456,7 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
   }
 // Split-K cost model (see choose_splits): fitted to split sweeps of small-M shapes (M 128..256,
 // N 4096..8192, K 4096..8192) on MI355X with streaming partial stores and 4-byte scale copies.
-constexpr float kSplitKtileUs = 0.54f, kSplitPartialUsPerMib = 0.22f;
+constexpr float kSplitKtileUs = 0.54f, kSplitPartialUsPerMib = 0.22f, kSplitFixedUs = 2.4f;
 constexpr int kMaxSplits = 16;
 static_assert(kMaxSplits <= kMaxFinishSplits, "the finish kernel sums at most kMaxFinishSplits partials");
 const KernelVariant kSharedA[8] = BSG_NVR_TABLE(Cfg128, true, "nvfp4_128x256_sharedA", kMaxSplits);
