@@ -5,5 +5,5 @@ by the library.  It shares no code with the HIP path.
 """
 from .oracle import (MX_BLOCK, NV_BLOCK, bits_to_f64, contract, decode_e2m1, decode_e4m3, decode_e8m0,
                      dequant, dequant_mxfp8, dequant_nvfp4, epilogue, reference, round_output,
-                     round_to_bf16_bits, round_to_f16_bits, silu_scalar, unpack_e2m1)
-from .tolerance import compare
+                     round_to_bf16_bits, round_to_f16_bits, unpack_e2m1)
+from .tolerance import accumulation_bound, compare, silu_kappa, silu_slope, silu_slope_max

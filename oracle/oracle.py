@@ -28,8 +28,6 @@ exact rational brute force).
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 MX_BLOCK = 32
@@ -211,7 +209,8 @@ def reference(p: dict, rows=None) -> dict:
 
     rows: optional index array; then only those rows of D are computed (all N
     columns), for sampled checks at full size.
-    Returns dict(bits=[r, N] uint16, y=fp64 before rounding, S=sum |a b|, acc=fp64 sum).
+    Returns dict(bits=[r, N] uint16, y=fp64 before rounding, x=alpha*acc + bias (the epilogue's
+    input), S=sum |a b|, acc=fp64 sum, fmt, K).
     """
     fmt, K = p["fmt"], p["K"]
     A, sA = p["A"], p["sA"]
@@ -221,12 +220,7 @@ def reference(p: dict, rows=None) -> dict:
     a = dequant(fmt, A, sA, K)
     b = dequant(fmt, p["B"], p["sB"], K)
     acc, S = contract(a, b)
+    x = epilogue(acc, p["alpha"], p["bias"], False)
     y = epilogue(acc, p["alpha"], p["bias"], p["silu"])
-    return dict(bits=round_output(y, p["out"]), y=y, S=S, acc=acc)
+    return dict(bits=round_output(y, p["out"]), y=y, x=x, S=S, acc=acc, fmt=fmt, K=K)
 
-
-def silu_scalar(x: float) -> float:
-    """SiLU of one fp64 scalar, x * sigmoid(x), for spot checks."""
-    if x < -700.0:
-        return -0.0 if x < 0 else 0.0
-    return x / (1.0 + math.exp(-x))
