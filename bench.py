@@ -1,34 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the block-scaled GEMM on one MI355X.
 
-Headline: MXFP8 GEMM M=N=K=4096 (inputs ~N(0,1) fp32, 5% of rows of A and of B scaled x1000,
-quantised per 32-K block to E4M3 with E8M0 scale 2^ceil(log2(amax/448))), fp32 accumulation,
-BF16 output, alpha = 0.5.  One step = one bsg_run call (plan created once; inputs resident in HBM).
-Reported value: whole-job TFLOP/s = 2*M*N*K / host wall time per step.
+Headline: MXFP8 GEMM M=N=K=8192 (inputs ~N(0,1) fp32 quantised per 32-K block to E4M3 with E8M0
+scale 2^ceil(log2(amax/448))), fp32 accumulation, fused epilogue D = SiLU(alpha * A B^T + bias)
+with bias ~N(0,1) fp32[N] and alpha = 1, FP16 output.  One step = one bsg_run call (plan created
+once; inputs resident in HBM).  value = whole-job TFLOP/s = 2*M*N*K / host wall time per step.
+roofline: the same flops / the kernel's average duration from HIP events on the launch stream over
+the timed steps, against the dense MX-FP8 peak (5.0 PFLOP/s).
 
-Also reported, in "extra": the other workloads (MXFP8 8192^3 fp16 with bias+SiLU, NVFP4
-128x8192x8192 bias+SiLU, MXFP8 256^3) and the looped small-M NVFP4 GEMM (M=256, N=K=4096, 10 input
-sets x 100 calls) as host wall time per call vs GPU time per call, direct and from HIP graphs.
+Also reported, in "extra" (each run before the headline, so the headline is timed on a warm device):
+MXFP8 4096^3 bf16 alpha 0.5 with 5% outlier rows, MXFP8 256^3, NVFP4 128x8192x8192 bias+SiLU, the
+K-tile-major scale layout on two workloads, and the looped small-M NVFP4 GEMM (M=256, N=K=4096, 10
+seeded input sets x 100 calls): host wall time per call vs GPU time per call, direct and from HIP
+graphs, the host's enqueue-only time, the empty-kernel dispatch period, and the oracle parity of all
+10 sets' outputs after the timed loops.
 
-The CPU baseline is the fp64 oracle (test infrastructure) timed on the host cores on a bounded sample
-of rows of the headline workload.
+CPU baseline: the fp64 oracle (test infrastructure) timed on the host cores on bounded samples of
+each workload; the headline's sample is rows of the 8192^3 problem.
 
-Scales are row-major by default (the ABI default).  --scale-layout ktile runs every workload on the
-library's K-tile-major scale layout instead (BSG_SCALES_KTILE; scales converted by bsg_pack_scales
-before timing, as the MXFP8 page's test swizzles its scales before the GEMM); the default run also
-reports the headline and the NVFP4 128x8192x8192 workload on that layout in "extra".
-
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-main] [--calibration-copy]
-                       [--scale-layout linear|ktile]
-       python bench.py --counters-from FETCH_CSV WRITE_CSV   (records HBM traffic from rocprofv3 passes)
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-main] [--scale-layout linear|ktile]
+       python bench.py --only-workload NAME [--steps K --warmup W] [--calibration-copy]
+                      (one workload only, for rocprofv3 runs; prints its timing)
+       python bench.py --counters-from FETCH_CSV WRITE_CSV --workload NAME
+                      (no GPU: record HBM traffic per kernel from two rocprofv3 --pmc passes)
        python bench.py --api-loop N   (N direct calls per workload only, for rocprofv3 --hip-trace)
-       python bench.py --only-workload NAME [--steps K --warmup W]   (one workload only, for
-                      rocprofv3 counter passes; prints its timing, not the benchmark line)
 """
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -38,30 +37,53 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"mxfp8": 5000.0, "nvfp4_fp4": 10100.0, "bf16": 2500.0}  # MI355X dense, published
+PEAK_TFLOPS = {"mxfp8": 5000.0, "nvfp4_fp4": 10100.0, "fp16": 2500.0}  # MI355X dense, published
 HBM_GBS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "mxfp8_4096_counters.json")
+HEADLINE = "mxfp8_8192_silu"
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Sources each workload's kernels are built from: committed counters are valid only for these bytes.
+_COMMON = ("common.h", "epilogue.h")
+KERNEL_SOURCES = {
+    "mxfp8_8192_silu": ("mxfp8_pp.hip",) + _COMMON,
+    "mxfp8_4096": ("mxfp8_pp.hip",) + _COMMON,
+    "nvfp4_128x8192x8192_silu": ("nvfp4_gemm.hip", "codec.h", "splitk.h") + _COMMON,
+    "nvfp4_256x4096x4096_loop": ("nvfp4_gemm.hip", "codec.h", "splitk.h") + _COMMON,
+}
 
 
-# Sources of the headline kernel (mxfp8_pp): committed counters are valid only for these bytes.
-HEADLINE_SOURCES = ("mxfp8_pp.hip", "common.h", "epilogue.h")
+def counters_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"{workload}_counters.json")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for name in HEADLINE_SOURCES:
+    for name in KERNEL_SOURCES[workload]:
         with open(os.path.join(ROOT, "block_scaled_precision_gemm_amd", "csrc", name), "rb") as fh:
             h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def write_counters(fetch_csv: str, write_csv: str) -> int:
-    """Turn two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; each over `bench.py --only-main
-    --calibration-copy`) into profiles/mxfp8_4096_counters.json.  FETCH_SIZE / WRITE_SIZE are scaled by
-    what they read for the 256 MiB device copy of known size."""
+def algorithmic_bytes(p: dict) -> int:
+    """Each operand byte read once, D written once: A, B, scales (+ bias) + 2 M N."""
+    M, N, K = p["M"], p["N"], p["K"]
+    if p["fmt"] == "mxfp8":
+        elems, scales = (M + N) * K, (M + N) * K // 32
+    else:
+        elems, scales = (M + N) * K // 2, (M + N) * K // 16
+    return elems + scales + (4 * N if p["bias"] is not None else 0) + 2 * M * N
+
+
+def write_counters(fetch_csv: str, write_csv: str, workload: str) -> int:
+    """Turn two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE; each over `bench.py --only-workload
+    <workload> --calibration-copy`) into profiles/<workload>_counters.json: HBM bytes per dispatch of
+    each kernel, FETCH_SIZE and WRITE_SIZE scaled by what they read for the 256 MiB device copy of
+    known size."""
     import csv
     import statistics
+
+    import seeded_inputs as si
 
     def per_kernel(path, counter):
         vals = {}
@@ -71,31 +93,47 @@ def write_counters(fetch_csv: str, write_csv: str) -> int:
         return {k: statistics.mean(v) for k, v in vals.items()}
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    gemm = [k for k in fetch if "mxfp8_pp_kernel" in k]
     copy = [k for k in fetch if "copyBuffer" in k]
-    if len(gemm) != 1 or len(copy) != 1:
-        print(f"expected one GEMM and one copy kernel, got {list(fetch)}", file=sys.stderr)
+    if len(copy) != 1:
+        print(f"expected one calibration copy kernel, got {list(fetch)}", file=sys.stderr)
         return 1
-    g, c = gemm[0], copy[0]
+    c = copy[0]
     n = float(1 << 28)
     rf, wf = n / (fetch[c] * 1024), n / (write[c] * 1024)
-    traffic = fetch[g] * 1024 * rf + write[g] * 1024 * wf
-    M = N = K = 4096
+    kernels = {}
+    for k in fetch:
+        if "bsg::" not in k or k not in write:  # the library's kernels only (not torch's fills or the copy)
+            continue
+        kernels[k] = {"fetch_kib_per_dispatch": fetch[k], "write_kib_per_dispatch": write[k],
+                      "traffic_bytes_per_dispatch": fetch[k] * 1024 * rf + write[k] * 1024 * wf}
+    p = si.workload(workload)
     out = {
-        "kernel": g, "workload": "MXFP8 4096^3 bf16 alpha 0.5",
-        "fetch_kib_per_dispatch": fetch[g], "write_kib_per_dispatch": write[g],
+        "workload": workload, "kernels": kernels,
+        "traffic_bytes_per_call": sum(v["traffic_bytes_per_dispatch"] for v in kernels.values()),
+        "algorithmic_bytes_per_call": algorithmic_bytes(p),
         "copy_calibration": {"bytes_read": n, "bytes_written": n, "fetch_kib": fetch[c], "write_kib": write[c],
                              "read_factor": rf, "write_factor": wf},
-        "traffic_bytes_per_launch": traffic,
-        "algorithmic_bytes_per_launch": M * K + N * K + (M + N) * K // 32 + 2 * M * N,
-        "source_hash": kernel_source_hash(),
-        "commands": [f"rocprofv3 --pmc {x} -f csv -d <repo>/gpurun_out/pmc_{x.lower()} -o run -- python3 <repo>/bench.py "
-                     "--only-main --steps 20 --warmup 5 --calibration-copy" for x in ("FETCH_SIZE", "WRITE_SIZE")],
+        "source_hash": kernel_source_hash(workload),
+        "commands": [f"rocprofv3 --pmc {x} -f csv -d <repo>/gpurun_out/pmc_{workload}_{x.lower()} -o run -- "
+                     f"python3 <repo>/bench.py --only-workload {workload} --steps 20 --warmup 20 --calibration-copy"
+                     for x in ("FETCH_SIZE", "WRITE_SIZE")],
     }
-    with open(COUNTERS, "w") as f:
+    with open(counters_path(workload), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
     return 0
+
+
+def traffic_from_counters(workload: str) -> float | None:
+    """HBM bytes per call from committed rocprofv3 --pmc counters, if taken on the current kernel sources."""
+    path = counters_path(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_hash") != kernel_source_hash(workload):
+        return None
+    return c.get("traffic_bytes_per_call")
 
 
 def log(msg: str) -> None:
@@ -119,13 +157,14 @@ def device_inputs(p: dict, scale_layout: str = "linear"):
     return d
 
 
-def time_gemm(p: dict, steps: int, warmup: int, stream, scale_layout: str = "linear") -> dict:
-    """Warm up, then time `steps` back-to-back calls on `stream` (host wall and HIP events)."""
+def time_gemm(p: dict, steps: int, warmup: int, stream, scale_layout: str = "linear", d: dict | None = None) -> dict:
+    """Warm up, then time `steps` back-to-back calls on `stream` (host wall and HIP events on that stream).
+    d: the problem's device inputs, if already uploaded."""
     import torch
     import block_scaled_precision_gemm_amd as bsg
     plan = bsg.Plan(p["fmt"], p["M"], p["N"], p["K"], out=p["out"], bias=p["bias"] is not None, silu=p["silu"],
                     scale_layout=scale_layout)
-    d = device_inputs(p, scale_layout)
+    d = d or device_inputs(p, scale_layout)
     args = (d["A"], d["B"], d["sA"], d["sB"], d["D"])
     kw = dict(alpha=float(p["alpha"]), bias=d["bias"], stream=stream)
     for _ in range(warmup):
@@ -148,12 +187,30 @@ def time_gemm(p: dict, steps: int, warmup: int, stream, scale_layout: str = "lin
                 tflops_wall=flops / (wall_ms * 1e-3) / 1e12, tflops_gpu=flops / (gpu_ms * 1e-3) / 1e12, flops=flops)
 
 
-def loop_bench(stream, n_sets: int = 10, calls: int = 100, scale_layout: str = "linear") -> dict:
-    """Looped small-M NVFP4 GEMM: n_sets fresh seeded input sets x `calls` back-to-back calls."""
+def roofline(name: str, p: dict, r: dict) -> dict:
+    """Roofline entry of a timed workload: MXFP8 against the MX-FP8 peak; NVFP4 against the fp16 MFMA
+    peak of its exact dequantised route (and, for reference, the MX-FP4 peak)."""
+    achieved = r["tflops_gpu"]
+    peak = PEAK_TFLOPS["mxfp8"] if p["fmt"] == "mxfp8" else PEAK_TFLOPS["fp16"]
+    out = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+           "frac": round(achieved / peak, 4), "traffic": traffic_from_counters(name) if name in KERNEL_SOURCES else None,
+           "kernel": r["variant"], "kernel_ms": round(r["gpu_ms"], 5), "flops_per_launch": r["flops"],
+           "algorithmic_bytes": algorithmic_bytes(p)}
+    if p["fmt"] == "nvfp4":
+        out["frac_of_mxfp4_peak"] = round(achieved / PEAK_TFLOPS["nvfp4_fp4"], 4)
+    return out
+
+
+def _rounded(d: dict, nd: int = 4) -> dict:
+    return {k: (round(v, nd) if isinstance(v, float) else v) for k, v in d.items() if k != "flops"}
+
+
+def loop_bench(stream, sets_host: list[dict], calls: int = 100, scale_layout: str = "linear") -> tuple[dict, list]:
+    """Looped small-M NVFP4 GEMM: len(sets_host) seeded input sets x `calls` back-to-back calls from C++,
+    direct and from HIP graphs, plus the empty-kernel dispatch floor.  Returns the timings and the
+    device sets, whose outputs loop_parity() checks afterwards."""
     import torch
     import block_scaled_precision_gemm_amd as bsg
-    import seeded_inputs as si
-    sets_host = [si.workload("nvfp4_256x4096x4096_loop", set_id=s) for s in range(n_sets)]
     p0 = sets_host[0]
     plan = bsg.Plan("nvfp4", p0["M"], p0["N"], p0["K"], out="bf16", scale_layout=scale_layout)
     sets = []
@@ -161,11 +218,13 @@ def loop_bench(stream, n_sets: int = 10, calls: int = 100, scale_layout: str = "
         d = device_inputs(p, scale_layout)
         d["alpha"] = float(p["alpha"])
         sets.append(d)
-    # warm-up (first-launch costs, caches)
-    bsg.bench_loop(plan, sets, 5, 0, stream)
-    direct_us = bsg.bench_loop(plan, sets, calls, 0, stream)
-    graph_us = bsg.bench_loop(plan, sets, calls, 1, stream)
-    # GPU time per call: HIP events around 1000 back-to-back calls on the same stream
+    n = len(sets) * calls
+    bsg.bench_loop(plan, sets, 5, 0, stream)  # warm-up (first-launch costs, caches)
+    for d in sets:
+        d["D"].fill_(0x7FFF)  # poison: each set's D must be rewritten by the timed loops
+    direct_us, direct_submit_us = bsg.bench_loop(plan, sets, calls, 0, stream, with_submit=True)
+    graph_us, graph_submit_us = bsg.bench_loop(plan, sets, calls, 1, stream, with_submit=True)
+    # GPU time per call: HIP events around n back-to-back calls on the launch stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -174,16 +233,37 @@ def loop_bench(stream, n_sets: int = 10, calls: int = 100, scale_layout: str = "
             plan.run(d["A"], d["B"], d["sA"], d["sB"], d["D"], alpha=d["alpha"], stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
-    n = n_sets * calls
     gpu_us = e0.elapsed_time(e1) * 1e3 / n
-    flops = 2.0 * p0["M"] * p0["N"] * p0["K"]
+    # the floor of any launch: empty kernels back to back, same stream, from C++
+    bsg.null_loop(100, stream)
+    null_wall_us, null_submit_us = bsg.null_loop(n, stream)
     info = plan.info()
     plan.close()
-    return dict(variant=info["variant"], calls=n, gpu_us_per_call=gpu_us,
+    flops = 2.0 * p0["M"] * p0["N"] * p0["K"]
+    return dict(variant=info["variant"], calls=n, kernel_us_per_call_events=gpu_us,
                 wall_us_per_call_direct=direct_us / n, wall_us_per_call_graph=graph_us / n,
+                submit_us_per_call_direct=direct_submit_us / n, submit_us_per_call_graph=graph_submit_us / n,
                 overhead_pct_direct=100.0 * (direct_us / n - gpu_us) / gpu_us,
                 overhead_pct_graph=100.0 * (graph_us / n - gpu_us) / gpu_us,
-                tflops_gpu=flops / (gpu_us * 1e-6) / 1e12)
+                null_kernel_period_us=null_wall_us / n, null_kernel_submit_us=null_submit_us / n,
+                launches_per_call=2 if info["workspace_bytes"] else 1,
+                tflops_gpu=flops / (gpu_us * 1e-6) / 1e12), sets
+
+
+def loop_parity(sets_host: list[dict], sets: list) -> tuple[list, float]:
+    """Every set's output after the timed loops, against the oracle; and the oracle's time per call
+    (the CPU baseline of this workload)."""
+    import numpy as np
+    from oracle import compare, reference
+    parity, oracle_s = [], []
+    for s, (p, d) in enumerate(zip(sets_host, sets)):
+        t0 = time.perf_counter()
+        ref = reference(p)
+        oracle_s.append(time.perf_counter() - t0)
+        rep = compare(d["D"].cpu().numpy().view(np.uint16), ref, p["alpha"], p["silu"], p["out"])
+        parity.append(dict(set=s, ok=rep["ok"], n_bad=rep["n_bad"], n_resolvable=rep["n_resolvable"],
+                           max_rel_resolvable=round(rep["max_rel_err"], 5)))
+    return parity, sum(oracle_s) / len(oracle_s)
 
 
 def api_loop(n: int, stream) -> int:
@@ -205,44 +285,35 @@ def api_loop(n: int, stream) -> int:
     return 0
 
 
-def cpu_baseline(p: dict, budget_s: float = 12.0) -> dict:
-    """The oracle as it stands, timed on host cores over row chunks of the workload until the budget."""
-    import numpy as np
+def blas_threads() -> int:
     from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+
+
+def cpu_oracle(p: dict, budget_s: float, chunk: int) -> dict:
+    """The oracle as it stands, timed on host cores over row chunks of the workload until the budget
+    (each call dequantises all of B again, as the oracle does)."""
+    import numpy as np
     import oracle
-    chunk = 256
-    rows_done, t_total = 0, 0.0
+    rows_done, t_total, chunks = 0, 0.0, 0
     while t_total < budget_s and rows_done < p["M"]:
         rows = np.arange(rows_done, min(rows_done + chunk, p["M"]))
         t0 = time.perf_counter()
         oracle.reference(p, rows=rows)
         t_total += time.perf_counter() - t0
         rows_done += len(rows)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        chunks += 1
     flops = 2.0 * rows_done * p["N"] * p["K"]
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 oracle (dequantise, A x B^T and sum|ab| via numpy/BLAS, epilogue, bf16 rounding) "
-                      f"on rows 0..{rows_done - 1} of the {p['M']}x{p['N']}x{p['K']} workload, "
-                      f"{t_total:.1f} s in {rows_done // chunk + (rows_done % chunk > 0)} chunks of {chunk} rows"}
-
-
-def traffic_from_counters(gpu_ms: float) -> dict | None:
-    """HBM bytes per launch from committed rocprofv3 --pmc counters, if taken on the current kernels."""
-    if not os.path.exists(COUNTERS):
-        return None
-    with open(COUNTERS) as f:
-        c = json.load(f)
-    if c.get("source_hash") != kernel_source_hash():
-        return None
-    return dict(bytes=c["traffic_bytes_per_launch"], gbs=c["traffic_bytes_per_launch"] / (gpu_ms * 1e-3) / 1e9)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "seconds": round(t_total, 3), "rows": rows_done,
+            "chunks": chunks}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--only-main", action="store_true", help="time the headline workload only (for profiling)")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-main", action="store_true", help="time the headline workload only")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run a device copy of known size (HBM counter calibration)")
     ap.add_argument("--api-loop", type=int, metavar="N",
@@ -254,10 +325,11 @@ def main() -> int:
     ap.add_argument("--scale-layout", choices=("linear", "ktile"), default="linear",
                     help="scale layout of every workload (default: row-major, the ABI default)")
     ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="no GPU run: write the headline kernel's HBM-traffic record from two rocprofv3 passes")
+                    help="no GPU run: write a workload's HBM-traffic record from two rocprofv3 passes")
+    ap.add_argument("--workload", default=HEADLINE, help="workload of --counters-from")
     args = ap.parse_args()
     if args.counters_from:
-        return write_counters(*args.counters_from)
+        return write_counters(*args.counters_from, args.workload)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
@@ -274,18 +346,9 @@ def main() -> int:
     stream = torch.cuda.Stream()
     if args.api_loop:
         return api_loop(args.api_loop, stream)
-    if args.only_workload:
-        r = time_gemm(si.workload(args.only_workload), args.steps, args.warmup, stream, args.scale_layout)
-        print(json.dumps({"workload": args.only_workload, "scale_layout": args.scale_layout,
-                          **{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}}), flush=True)
-        return 0
-
-    log("generating the headline workload (MXFP8 4096^3)")
-    p = si.workload("mxfp8_4096")
     lay = args.scale_layout
-    main_r = time_gemm(p, args.steps, args.warmup, stream, lay)
-    log(f"main: {main_r}")
-    if args.calibration_copy:
+
+    def calibration_copy():
         n = 1 << 28  # 256 MiB read + 256 MiB written per copy
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -294,44 +357,66 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"calibration copy: 5 x {n} bytes")
 
-    extra = {}
+    if args.only_workload:
+        r = time_gemm(si.workload(args.only_workload), args.steps, args.warmup, stream, lay)
+        if args.calibration_copy:
+            calibration_copy()
+        print(json.dumps({"workload": args.only_workload, "scale_layout": lay, **_rounded(r, 5)}), flush=True)
+        return 0
+
+    # All inputs are generated on the host first, and the GPU phase then runs without idle gaps (an
+    # idle GPU drops its clock, and the next kernels pay the ramp); oracle work comes after it.
+    extra, cpu_per_config = {}, {}
+    workloads = {}
+    log("generating the workloads on the host")
+    p = si.workload(HEADLINE)
+    p_dev = device_inputs(p, lay)
     if not args.only_main:
-        # warm-up lengths cover the clock / power transient of the first few hundred calls
-        for name, steps, warm in (("mxfp8_8192_silu", 30, 60), ("nvfp4_128x8192x8192_silu", 200, 400),
+        for name in ("mxfp8_4096", "nvfp4_128x8192x8192_silu", "mxfp8_256"):
+            workloads[name] = si.workload(name)
+        loop_sets = [si.workload("nvfp4_256x4096x4096_loop", set_id=s) for s in range(10)]
+        # fixed warm-up lengths cover the clock / power transient of a fresh process
+        for name, steps, warm in (("mxfp8_4096", 200, 400), ("nvfp4_128x8192x8192_silu", 200, 400),
                                   ("mxfp8_256", 500, 500)):
-            log(f"workload {name}")
-            q = si.workload(name)
+            q = workloads[name]
             r = time_gemm(q, steps, warm, stream, lay)
-            peak = PEAK_TFLOPS["mxfp8"] if q["fmt"] == "mxfp8" else PEAK_TFLOPS["nvfp4_fp4"]
-            r["frac_of_mx_peak"] = r["tflops_gpu"] / peak
-            if q["fmt"] == "nvfp4":
-                r["frac_of_bf16_peak"] = r["tflops_gpu"] / PEAK_TFLOPS["bf16"]
-            extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "flops"}
+            extra[name] = {**_rounded(r), "roofline": roofline(name, q, r)}
             log(f"{name}: {extra[name]}")
         log("looped NVFP4 256x4096x4096, 10 sets x 100 calls")
-        extra["nvfp4_256x4096x4096_loop"] = {k: (round(v, 3) if isinstance(v, float) else v)
-                                             for k, v in loop_bench(stream, scale_layout=lay).items()}
-        log(f"loop: {extra['nvfp4_256x4096x4096_loop']}")
+        lp, loop_dev = loop_bench(stream, loop_sets, scale_layout=lay)
         if lay == "linear":
-            for name, steps, warm in (("mxfp8_4096", args.steps, 100), ("nvfp4_128x8192x8192_silu", 200, 100)):
-                q = p if name == "mxfp8_4096" else si.workload(name)
-                r = time_gemm(q, steps, warm, stream, "ktile")
-                extra[name + "_ktile_scales"] = {k: (round(v, 4) if isinstance(v, float) else v)
-                                                 for k, v in r.items() if k != "flops"}
+            for name, steps, warm in (("mxfp8_4096", 200, 100), ("nvfp4_128x8192x8192_silu", 200, 100)):
+                r = time_gemm(workloads[name], steps, warm, stream, "ktile")
+                extra[name + "_ktile_scales"] = _rounded(r)
                 log(f"{name} on K-tile-major scales: {extra[name + '_ktile_scales']}")
+
+    main_r = time_gemm(p, args.steps, args.warmup, stream, lay, d=p_dev)
+    log(f"main: {main_r}")
 
     cpu = None
     if not args.only_main:
-        log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(p)
+        parity, oracle_call_s = loop_parity(loop_sets, loop_dev)
+        lp.update(parity_all_sets_ok=all(x["ok"] for x in parity), parity=parity)
+        extra["nvfp4_256x4096x4096_loop"] = _rounded(lp, 3)
+        log(f"loop: {extra['nvfp4_256x4096x4096_loop']}")
+        cpu_per_config["nvfp4_256x4096x4096_loop"] = {"seconds_per_call": round(oracle_call_s, 3),
+                                                      "sample": "one full call (all 256 rows) per input set, 10 sets"}
+        log("timing the CPU oracle on bounded samples")
+        threads, cores = blas_threads(), os.cpu_count()
+        for name, budget, chunk in (("mxfp8_256", 2.0, 256), ("mxfp8_4096", 4.0, 256),
+                                    ("nvfp4_128x8192x8192_silu", 6.0, 128)):
+            c = cpu_oracle(workloads[name], budget, chunk)
+            cpu_per_config[name] = {**c, "value": round(c["value"], 4)}
+        c = cpu_oracle(p, 12.0, 256)
+        cpu_per_config[HEADLINE] = {**c, "value": round(c["value"], 4)}
+        cpu = {"value": round(c["value"], 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "host_cpu_count": cores,
+               "sample": f"fp64 oracle (decode, exact dequantisation, A x B^T and sum|ab| as fp64 BLAS matmuls, "
+                         f"fp64 epilogue, one fp16 rounding) on rows 0..{c['rows'] - 1} of the 8192^3 workload "
+                         f"in {c['chunks']} chunks ({c['seconds']} s; each chunk dequantises all of B again)"}
+        extra["cpu_oracle_per_config"] = {"blas_threads": threads, "host_cpu_count": cores, **cpu_per_config}
 
-    achieved = main_r["tflops_gpu"]
-    peak = PEAK_TFLOPS["mxfp8"]
-    tr = traffic_from_counters(main_r["gpu_ms"])
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None if tr is None else tr["bytes"],
-                "kernel": main_r["variant"], "kernel_ms": round(main_r["gpu_ms"], 5),
-                "flops_per_launch": main_r["flops"]}
+    rl = roofline(HEADLINE, p, main_r)
     line = {
         "metric": "block-scaled GEMM TFLOPS (% of MX MFMA peak) + per-call loop us vs kernel us",
         "value": round(main_r["tflops_wall"], 2),
@@ -344,11 +429,12 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp8_e4m3",
-        "data": "synthetic (seeded N(0,1), 5% rows x1000, quantised to MXFP8 on the host)",
-        "config": {"workload": "MXFP8 GEMM M=N=K=4096, E4M3 + E8M0/32, alpha=0.5, bf16 out, 5% outlier rows",
-                   "M": p["M"], "N": p["N"], "K": p["K"], "out": "bf16", "alpha": 0.5,
+        "data": "synthetic (seeded N(0,1) operands and bias, quantised to MXFP8 on the host)",
+        "config": {"workload": "MXFP8 GEMM M=N=K=8192, E4M3 + E8M0 per 32 K, D = SiLU(alpha*A B^T + bias), "
+                               "bias fp32[N], alpha=1, fp16 out",
+                   "M": p["M"], "N": p["N"], "K": p["K"], "out": "f16", "alpha": 1.0, "epilogue": "bias+silu",
                    "scale_layout": "row-major" if lay == "linear" else "K-tile-major (packed before timing)"},
-        "roofline": roofline,
+        "roofline": rl,
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "decode_nvfp4_f16",
+__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "null_loop", "decode_nvfp4_f16",
            "FORMATS", "OUT_DTYPES", "SCALE_LAYOUTS", "abi_version", "packed_strides", "Problem", "PROBLEM_V1_SIZE", "PROBLEM_V2_SIZE",
            "pack_scales", "scales_ktile_bytes"]
 
@@ -96,7 +96,10 @@ _SIGNATURES = {
     "bsg_bench_loop": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_VP), ctypes.c_int,
-                                      ctypes.c_int, _VP, ctypes.POINTER(ctypes.c_double)]),
+                                      ctypes.c_int, _VP, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_double)]),
+    "bsg_bench_null_loop": (ctypes.c_int, [ctypes.c_int, _VP, ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_double)]),
 }
 
 
@@ -217,8 +220,9 @@ class Plan:
         self.close()
 
 
-def bench_loop(plan: Plan, sets: list[dict], calls_per_set: int, mode: int, stream) -> float:
-    """Native loop of len(sets) * calls_per_set bsg_run calls; returns the host wall time in us.
+def bench_loop(plan: Plan, sets: list[dict], calls_per_set: int, mode: int, stream, with_submit: bool = False):
+    """Native loop of len(sets) * calls_per_set bsg_run calls; returns the host wall time in us
+    (with_submit: the pair (wall, enqueue-only time) in us).
 
     Each set is a dict with A, B, sA, sB, D, alpha and optional bias.  mode 0 = direct calls,
     mode 1 = one HIP graph per set (captured outside the timed region) replayed.
@@ -228,10 +232,18 @@ def bench_loop(plan: Plan, sets: list[dict], calls_per_set: int, mode: int, stre
     arr = lambda key: (_VP * n)(*[_ptr(s.get(key)) for s in sets])  # noqa: E731
     alphas = (ctypes.c_float * n)(*[float(s["alpha"]) for s in sets])
     has_bias = any(s.get("bias") is not None for s in sets)
-    wall = ctypes.c_double()
+    wall, submit = ctypes.c_double(), ctypes.c_double()
     _check(lib.bsg_bench_loop(plan._h, n, arr("A"), arr("B"), arr("sA"), arr("sB"), arr("bias") if has_bias else None,
-                              alphas, arr("D"), calls_per_set, mode, _stream(stream), ctypes.byref(wall)))
-    return wall.value
+                              alphas, arr("D"), calls_per_set, mode, _stream(stream), ctypes.byref(wall),
+                              ctypes.byref(submit)))
+    return (wall.value, submit.value) if with_submit else wall.value
+
+
+def null_loop(n: int, stream) -> tuple[float, float]:
+    """n back-to-back launches of an empty kernel from C++: (wall us, enqueue-only us)."""
+    wall, submit = ctypes.c_double(), ctypes.c_double()
+    _check(load_library().bsg_bench_null_loop(n, _stream(stream), ctypes.byref(wall), ctypes.byref(submit)))
+    return wall.value, submit.value
 
 
 def decode_nvfp4_f16(packed, scale_codes, out_f16, n_elements: int, stream=None) -> None:

@@ -18,6 +18,7 @@
 
 #include "bsg.h"
 #include "common.h"
+#include "plan.h"
 
 namespace bsg {
 
@@ -34,21 +35,6 @@ void set_error(const char* fmt, ...) {
 }
 
 }  // namespace bsg
-
-struct bsg_plan_s {
-  uint32_t magic;
-  bsg_problem problem;
-  bsg::GemmArgs args;  // template: shapes and tile counts; pointers patched per call
-  bsg::LaunchFn launch;
-  dim3 grid, block;
-  uint32_t lds_bytes;
-  bool needs_bias;
-  int device;
-  char variant[64];
-  int tile_m, tile_n, tile_k;
-  void* workspace;          // device memory owned by the plan (split-K partials), or null
-  uint64_t workspace_bytes;
-};
 
 namespace {
 
@@ -202,7 +188,8 @@ bsg_status validate(const bsg_problem* p) {
     return BSG_ERR_SHAPE;
   }
   if (p->K % 32 != 0) {
-    set_error("NVFP4 K %% 32 == 16 is not covered by a compiled kernel (K = %lld)", (long long)p->K);
+    set_error("NVFP4 K %% 32 == 16 is not covered by a compiled kernel (K = %lld): packed rows would be only 8-byte "
+              "aligned; pad K to a multiple of 32 with zero elements", (long long)p->K);
     return BSG_ERR_UNSUPPORTED;
   }
   if (p->lda < p->K || p->ldb < p->K || p->ldd < p->N || p->lda > lim || p->ldb > lim || p->ldd > lim) {
@@ -260,12 +247,18 @@ const char* bsg_status_string(bsg_status s) {
   return "BSG_ERR_UNKNOWN";
 }
 
-bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
-  if (!problem || !out_plan) {
-    set_error("null problem or out_plan");
+}  // extern "C"
+
+namespace bsg {
+
+// Everything bsg_plan_create does except allocating: validation, variant choice, launch shape and the
+// argument template, written into *plan (caller-owned storage).  The split-K workspace size is
+// plan->workspace_bytes; plan->args.ws is left null for the caller to point at a workspace.
+bsg_status build_plan(const bsg_problem* problem, bsg_plan_s* plan) {
+  if (!problem || !plan) {
+    set_error("null problem or plan");
     return BSG_ERR_NULL;
   }
-  *out_plan = nullptr;
   bsg_problem prob;
   bsg_status st = normalize(problem, &prob);
   if (st != BSG_OK) return st;
@@ -296,11 +289,7 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   }
   const bsg::KernelVariant& v = table[bsg::variant_index(out, bias, silu)];
 
-  bsg_plan_s* plan = new (std::nothrow) bsg_plan_s();
-  if (!plan) {
-    set_error("out of host memory");
-    return BSG_ERR_ALLOC;
-  }
+  memset((void*)plan, 0, sizeof(*plan));
   plan->magic = bsg::kPlanMagic;
   plan->problem = *problem;
   plan->problem.device = dev;
@@ -314,7 +303,6 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   snprintf(plan->variant, sizeof(plan->variant), "%s_%s%s%s", v.name, out == bsg::Out::F16 ? "f16" : "bf16",
            bias ? "_bias" : "", silu ? "_silu" : "");
   bsg::GemmArgs& a = plan->args;
-  memset(&a, 0, sizeof(a));
   a.M = (int)problem->M;
   a.N = (int)problem->N;
   a.K = (int)problem->K;
@@ -333,26 +321,17 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
   a.row_a = (int)(problem->lda / elem_den);
   a.row_b = (int)(problem->ldb / elem_den);
   a.ldd = (int)problem->ldd;
-  if (a.splits > 1) {
-    const size_t bytes =
-        (size_t)problem->batch * a.splits * (size_t)problem->M * (size_t)problem->N * sizeof(float);
-    st = device_alloc(dev, bytes, &plan->workspace);
-    if (st != BSG_OK) {
-      delete plan;
-      return st;
-    }
-    plan->workspace_bytes = bytes;
-    a.ws = (float*)plan->workspace;
-  }
+  if (a.splits > 1)
+    plan->workspace_bytes =
+        (uint64_t)problem->batch * a.splits * (uint64_t)problem->M * (uint64_t)problem->N * sizeof(float);
   plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n * a.splits), 1, (unsigned)problem->batch)
                              : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, (unsigned)problem->batch);
   plan->block = dim3((unsigned)v.block_threads, 1, 1);
-  *out_plan = plan;
   return BSG_OK;
 }
 
-static inline bsg_status run_impl(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB,
-                                  const float* bias, float alpha, const float* alpha_dev, void* D, void* stream) {
+bsg_status launch_plan(const bsg_plan_s* plan, const void* A, const void* B, const void* sA, const void* sB,
+                       const float* bias, float alpha, const float* alpha_dev, void* D, void* stream) {
   if (!plan || plan->magic != bsg::kPlanMagic) {
     set_error("invalid plan");
     return BSG_ERR_NULL;
@@ -361,9 +340,14 @@ static inline bsg_status run_impl(bsg_plan plan, const void* A, const void* B, c
     set_error("null operand pointer (A=%p B=%p sA=%p sB=%p D=%p bias=%p)", A, B, sA, sB, D, (const void*)bias);
     return BSG_ERR_NULL;
   }
-  if ((((uintptr_t)A | (uintptr_t)B | (uintptr_t)D) & 15u) || (((uintptr_t)sA | (uintptr_t)sB) & 3u)) {
-    set_error("A, B and D must be 16-byte aligned and sA, sB 4-byte aligned (A=%p B=%p D=%p sA=%p sB=%p)", A, B,
-              D, sA, sB);
+  if (plan->workspace_bytes > 0 && !plan->args.ws) {
+    set_error("plan has no split-K workspace");
+    return BSG_ERR_NULL;
+  }
+  const uintptr_t bias_bits = plan->needs_bias ? (uintptr_t)bias : 0;
+  if ((((uintptr_t)A | (uintptr_t)B | (uintptr_t)D) & 15u) || (((uintptr_t)sA | (uintptr_t)sB | bias_bits) & 3u)) {
+    set_error("A, B and D must be 16-byte aligned and sA, sB, bias 4-byte aligned (A=%p B=%p D=%p sA=%p sB=%p "
+              "bias=%p)", A, B, D, sA, sB, (const void*)bias);
     return BSG_ERR_ALIGN;
   }
   bsg::GemmArgs a = plan->args;
@@ -383,9 +367,37 @@ static inline bsg_status run_impl(bsg_plan plan, const void* A, const void* B, c
   return BSG_OK;
 }
 
+}  // namespace bsg
+
+extern "C" {
+
+bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan) {
+  if (!problem || !out_plan) {
+    set_error("null problem or out_plan");
+    return BSG_ERR_NULL;
+  }
+  *out_plan = nullptr;
+  bsg_plan_s* plan = new (std::nothrow) bsg_plan_s();
+  if (!plan) {
+    set_error("out of host memory");
+    return BSG_ERR_ALLOC;
+  }
+  bsg_status st = bsg::build_plan(problem, plan);
+  if (st == BSG_OK && plan->workspace_bytes > 0) {
+    st = device_alloc(plan->device, (size_t)plan->workspace_bytes, &plan->workspace);
+    plan->args.ws = (float*)plan->workspace;
+  }
+  if (st != BSG_OK) {
+    delete plan;
+    return st;
+  }
+  *out_plan = plan;
+  return BSG_OK;
+}
+
 bsg_status bsg_run(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB, const float* bias,
                    float alpha, void* D, void* stream) {
-  return run_impl(plan, A, B, sA, sB, bias, alpha, nullptr, D, stream);
+  return bsg::launch_plan(plan, A, B, sA, sB, bias, alpha, nullptr, D, stream);
 }
 
 bsg_status bsg_run_alpha_ptr(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB,
@@ -394,7 +406,7 @@ bsg_status bsg_run_alpha_ptr(bsg_plan plan, const void* A, const void* B, const 
     set_error("null alpha_dev");
     return BSG_ERR_NULL;
   }
-  return run_impl(plan, A, B, sA, sB, bias, 0.0f, alpha_dev, D, stream);
+  return bsg::launch_plan(plan, A, B, sA, sB, bias, 0.0f, alpha_dev, D, stream);
 }
 
 bsg_status bsg_plan_destroy(bsg_plan plan) {

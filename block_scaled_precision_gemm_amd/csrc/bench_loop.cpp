@@ -23,7 +23,7 @@ bsg_status hip_fail(const char* what, hipError_t e) {
 extern "C" bsg_status bsg_bench_loop(bsg_plan plan, int n_sets, const void* const* A, const void* const* B,
                                      const void* const* sA, const void* const* sB, const float* const* bias,
                                      const float* alpha, void* const* D, int calls_per_set, int mode, void* stream,
-                                     double* wall_us) {
+                                     double* wall_us, double* submit_us) {
   if (!plan || !A || !B || !sA || !sB || !alpha || !D || !wall_us) {
     bsg::set_error("null argument");
     return BSG_ERR_NULL;
@@ -45,9 +45,11 @@ extern "C" bsg_status bsg_bench_loop(bsg_plan plan, int n_sets, const void* cons
         const bsg_status st = bsg_run(plan, A[i], B[i], sA[i], sB[i], bias_of(i), alpha[i], D[i], stream);
         if (st != BSG_OK) return st;
       }
+    const auto ts = std::chrono::steady_clock::now();
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail("hipStreamSynchronize", e);
     const auto t1 = std::chrono::steady_clock::now();
     *wall_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+    if (submit_us) *submit_us = std::chrono::duration<double, std::micro>(ts - t0).count();
     return BSG_OK;
   }
 
@@ -86,9 +88,11 @@ extern "C" bsg_status bsg_bench_loop(bsg_plan plan, int n_sets, const void* cons
     const auto t0 = std::chrono::steady_clock::now();
     for (int i = 0; i < n_sets && result == BSG_OK; ++i)
       if ((e = hipGraphLaunch(execs[i], s)) != hipSuccess) result = hip_fail("hipGraphLaunch", e);
+    const auto ts = std::chrono::steady_clock::now();
     if ((e = hipStreamSynchronize(s)) != hipSuccess && result == BSG_OK) result = hip_fail("hipStreamSynchronize", e);
     const auto t1 = std::chrono::steady_clock::now();
     *wall_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+    if (submit_us) *submit_us = std::chrono::duration<double, std::micro>(ts - t0).count();
   }
   for (hipGraphExec_t x : execs)
     if (x) hipGraphExecDestroy(x);

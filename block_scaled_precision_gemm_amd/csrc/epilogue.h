@@ -9,13 +9,29 @@
 
 namespace bsg {
 
-// SiLU as y * rcp(1 + exp(-y)) with the hardware exp2 and reciprocal (each about 1 ulp of fp32):
-// far below the bf16 / fp16 rounding that follows, and a handful of VALU operations instead of an
-// IEEE division.  Large -y gives exp = inf, rcp(inf) = 0 and y * 0 = -0.
-template <bool SILU>
+// SiLU(y) = y / (1 + e^-y) with the hardware exp2 and reciprocal (each about 1 ulp of fp32, far below
+// the bf16 / fp16 rounding that follows).
+// * FP16 output: y * rcp(1 + e^-y).  Where e^-y overflows (y < -88.7) this gives -0, which is also
+//   the fp16 rounding of SiLU(y) there (|SiLU(y)| < 2^-25 from y ~ -21 down).
+// * BF16 output, whose range is fp32's: SiLU's negative tail is a bf16 subnormal down to y ~ -97,
+//   so e^-y must not overflow.  For y < 0 both denominator terms are scaled by c = 2^-64:
+//   SiLU(y) = (y * rcp(c + c e^-y)) * c, with c e^-y = 2^(-y log2 e - 64) finite down to y ~ -132
+//   (below, rcp(inf) = 0, and SiLU(y) rounds to zero anyway); c = 1 for y >= 0.  The final
+//   multiply by c rounds once into fp32's subnormal range.
+template <bool SILU, Out O>
 __device__ __forceinline__ float epi_value(float acc, float alpha, float bias) {
   float y = __builtin_fmaf(alpha, acc, bias);
-  if constexpr (SILU) y = y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+  if constexpr (SILU) {
+    constexpr float kLog2e = 1.44269504088896341f, kTwoM64 = 5.42101086242752217e-20f;  // 2^-64
+    if constexpr (O == Out::F16) {
+      y = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * kLog2e));
+    } else {
+      const bool neg = y < 0.0f;
+      const float c = neg ? kTwoM64 : 1.0f;
+      const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(-y, kLog2e, neg ? -64.0f : 0.0f));
+      y = (y * __builtin_amdgcn_rcpf(c + v)) * c;
+    }
+  }
   return y;
 }
 

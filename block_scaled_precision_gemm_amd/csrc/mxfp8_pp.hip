@@ -320,18 +320,18 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
       const int c0 = 32 * j + 8 * g + 4 * h;
       float bv[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (BIAS) {
-        if (nw + c0 < p.N) {
-          const v4f b4 = *(const v4f*)(p.bias + nw + c0);
-          bv[0] = b4[0]; bv[1] = b4[1]; bv[2] = b4[2]; bv[3] = b4[3];
+        if (nw + c0 < p.N) {  // bias is 4-byte aligned (the ABI's promise): four dword loads
+          const float* b = p.bias + nw + c0;
+          bv[0] = b[0]; bv[1] = b[1]; bv[2] = b[2]; bv[3] = b[3];
         }
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const v16f& a = acc[i][j];
-        const uint32_t lo = pack2_out<O>(epi_value<SILU>(a[4 * g + 0], alpha, bv[0]),
-                                         epi_value<SILU>(a[4 * g + 1], alpha, bv[1]));
-        const uint32_t hi = pack2_out<O>(epi_value<SILU>(a[4 * g + 2], alpha, bv[2]),
-                                         epi_value<SILU>(a[4 * g + 3], alpha, bv[3]));
+        const uint32_t lo = pack2_out<O>(epi_value<SILU, O>(a[4 * g + 0], alpha, bv[0]),
+                                         epi_value<SILU, O>(a[4 * g + 1], alpha, bv[1]));
+        const uint32_t hi = pack2_out<O>(epi_value<SILU, O>(a[4 * g + 2], alpha, bv[2]),
+                                         epi_value<SILU, O>(a[4 * g + 3], alpha, bv[3]));
         *(uint2*)(eb + (32 * i + r) * EPI_ROW + 2 * c0) = make_uint2(lo, hi);
       }
     }

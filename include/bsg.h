@@ -106,7 +106,13 @@ typedef struct bsg_problem {
   int32_t format;       /* bsg_format */
   int32_t out_dtype;    /* bsg_out_dtype */
   uint32_t flags;       /* BSG_EPI_*, BSG_SCALES_KTILE */
-  int64_t M, N, K;      /* M >= 1; N >= 16, N % 16 == 0; K >= 32, K % 32 == 0 (MXFP8) or K % 16 == 0 (NVFP4) */
+  int64_t M, N, K;      /* M >= 1; N >= 16, N % 16 == 0; K >= 32, K % 32 == 0 (MXFP8) or K % 16 == 0 (NVFP4).
+                         * NVFP4 with K % 32 == 16 is a valid shape that no compiled kernel covers
+                         * (BSG_ERR_UNSUPPORTED): a packed row is then K/2 == 8 (mod 16) bytes long, so
+                         * rows after the first are only 8-byte aligned, and every kernel moves
+                         * operand rows in 16-byte pieces (the 32-element FP4 alignment that the
+                         * CUTLASS kernels of the issue #3003 page also require).  Pad K to a multiple
+                         * of 32 with zero elements (zero scale codes) to run such a problem. */
   int32_t device;       /* HIP device ordinal; -1 = the current device at create time */
   /* Batched GEMM (ABI 2): `batch` independent problems of the same shape in one launch.  Problem z
    * (0 <= z < batch) reads A + z*stride_a, B + z*stride_b, sA + z*stride_sa, sB + z*stride_sb and
@@ -150,7 +156,8 @@ bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan);
 
 /* Enqueue D = epi(alpha * A x B^T (+ bias)) on `stream` (a hipStream_t; NULL = the null stream).
  * A, B, sA, sB, D: device pointers laid out as described at the top of this file; A, B and D must be
- * 16-byte aligned, sA and sB 4-byte aligned.  bias: device float[N], required iff the plan has BSG_EPI_BIAS (ignored otherwise).
+ * 16-byte aligned, sA and sB 4-byte aligned.  bias: device float[N], 4-byte aligned, required iff the plan has
+ * BSG_EPI_BIAS (ignored otherwise).
  * alpha: host fp32 value.  Returns after enqueueing (asynchronous).  Errors: BSG_ERR_NULL,
  * BSG_ERR_ALIGN, BSG_ERR_HIP (launch failure). */
 bsg_status bsg_run(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB,

@@ -22,9 +22,19 @@ def _check(p, rows=None, rel=1e-2):
     if rows is not None:
         D = D[rows]
     rep = compare(D, ref, p["alpha"], p["silu"], p["out"], rel=rel)
-    print(f"[parity] {p['fmt']} {p['M']}x{p['N']}x{p['K']} {p['out']} max_rel={rep['max_rel_err']:.3g} "
-          f"max_err/S={rep['max_err_over_S']:.3g} by_floor={rep['n_passed_by_floor']}/{rep['n']}", flush=True)
+    print(f"[parity] {p['fmt']} {p['M']}x{p['N']}x{p['K']} {p['out']} resolvable={rep['n_resolvable']}/{rep['n']} "
+          f"max_rel(resolvable)={rep['max_rel_err']:.3g} max_err/S={rep['max_err_over_S']:.3g} "
+          f"by_floor={rep['n_passed_by_floor']}", flush=True)
     assert rep["ok"], rep
+    return rep
+
+
+def _check_workload(p, rows=None, min_resolvable=0.1):
+    """A benchmark workload: the comparison rule, and the 1e-2 relative bar on the resolvable entries
+    (sums that keep >= 2^-6 of their absolute mass, well-conditioned epilogue) asserted on their own."""
+    rep = _check(p, rows=rows)
+    assert rep["n_resolvable"] >= min_resolvable * rep["n"], rep
+    assert rep["max_rel_err"] <= 1e-2, rep
     return rep
 
 
@@ -110,33 +120,35 @@ def test_large_mxfp8_sampled(shape, epi):
 
 
 def test_config_mxfp8_256():
-    _check(si.workload("mxfp8_256"))
+    _check_workload(si.workload("mxfp8_256"))
 
 
 def test_config_mxfp8_4096_sampled_rows():
     p = si.workload("mxfp8_4096")
     rows = np.unique(np.concatenate([np.arange(0, 4096, 97), [4095]]))
-    _check(p, rows=rows)
+    _check_workload(p, rows=rows)
 
 
 def test_config_mxfp8_8192_silu_sampled_rows():
     p = si.workload("mxfp8_8192_silu")
     rows = np.unique(np.concatenate([np.arange(0, 8192, 331), [8191]]))
-    _check(p, rows=rows)
+    _check_workload(p, rows=rows)
 
 
 def test_config_nvfp4_128x8192x8192_full():
-    _check(si.workload("nvfp4_128x8192x8192_silu"))
+    _check_workload(si.workload("nvfp4_128x8192x8192_silu"))
 
 
 def test_config_nvfp4_256x4096x4096_all_sets():
     plan = None
-    for s in range(3):
+    for s in range(10):
         p = si.workload("nvfp4_256x4096x4096_loop", set_id=s)
         plan = plan or make_plan(p)
         D = run(p, plan=plan)
         rep = compare(D, reference(p), p["alpha"], p["silu"], p["out"])
-        assert rep["ok"], (s, rep)
+        print(f"[parity] nvfp4 256x4096x4096 set {s}: resolvable={rep['n_resolvable']}/{rep['n']} "
+              f"max_rel(resolvable)={rep['max_rel_err']:.3g}", flush=True)
+        assert rep["ok"] and rep["n_resolvable"] >= 0.1 * rep["n"], (s, rep)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
@@ -182,18 +194,48 @@ def test_deterministic_and_alpha_ptr_matches():
 
 
 def test_e8m0_extreme_scales():
-    # one nonzero product per row: A[i, 0] = B[j, 0] = 1.0, sA[i, 0] sweeps codes 1..254, sB = 127
-    M, N, K = 254, 16, 32
+    # one nonzero product per entry: A[i, 0] = B[j, 0] = 1.0; sA[i, 0] sweeps every E8M0 code 0..255
+    # (0 = 2^-127, 255 = NaN) against sB in {2^-1, 2^0, 2^1}, so products span 2^-128 .. 2^128 (fp32
+    # subnormals and overflow to inf included) and a NaN scale code reaches the MFMA
+    M, N, K = 256, 48, 32
     A = np.zeros((M, K), np.uint8)
     A[:, 0] = 0x38
     B = np.zeros((N, K), np.uint8)
     B[:, 0] = 0x38
-    sA = np.arange(1, 255, dtype=np.uint8)[:, None]
-    sB = np.full((N, 1), 127, np.uint8)
+    sA = np.arange(0, 256, dtype=np.uint8)[:, None]
+    sB = (126 + np.arange(N) % 3).astype(np.uint8)[:, None]
     p = dict(fmt="mxfp8", M=M, N=N, K=K, A=A, B=B, sA=sA, sB=sB, alpha=np.float32(1), bias=None, silu=False,
              out="bf16")
     D = run(p)
-    assert np.array_equal(D, reference(p)["bits"])
+    R = reference(p)["bits"]
+    nan_d, nan_r = (D & 0x7FFF) > 0x7F80, (R & 0x7FFF) > 0x7F80
+    assert nan_r[255].all() and not nan_r[:255].any()
+    assert np.array_equal(nan_d, nan_r), f"NaN pattern differs: rows {np.unique(np.argwhere(nan_d != nan_r)[:, 0])}"
+    diff = (D != R) & ~nan_r
+    assert not diff.any(), [(int(i), int(j), hex(D[i, j]), hex(R[i, j])) for i, j in np.argwhere(diff)[:8]]
+
+
+def test_bias_four_byte_offset_on_large_mxfp8_kernel():
+    # the ABI promises only 4-byte bias alignment: a bias at a 4-byte offset gives the same bits as an
+    # aligned copy, on the large-shape kernel (whose epilogue reads 4 consecutive bias values per lane)
+    p = si.problem("mxfp8", 4096, 4096, 512, seed=31, bias=True, silu=True, out="f16", alpha=0.5)
+    plan = make_plan(p)
+    assert _is_large_kernel(plan.info()), plan.info()
+    dev = to_device(p)
+    D0 = run(p, plan=plan, dev=dev)
+    shifted = torch.zeros(p["N"] + 4, dtype=torch.float32, device="cuda")
+    shifted[1:p["N"] + 1] = dev["bias"]
+    dev["D"].fill_(0x7FFF)
+    plan.run(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha=float(p["alpha"]),
+             bias=shifted.data_ptr() + 4)
+    torch.cuda.synchronize()
+    D1 = dev["D"].cpu().numpy().view(np.uint16)
+    assert np.array_equal(D0, D1)
+    rows = _band_rows(4096)
+    assert compare(D1[rows], reference(p, rows=rows), p["alpha"], True, "f16")["ok"]
+    with pytest.raises(bsg.BsgError) as e:
+        plan.run(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha=1.0, bias=shifted.data_ptr() + 2)
+    assert e.value.status_name == "BSG_ERR_ALIGN"
 
 
 def test_errors_reported_without_launch():
