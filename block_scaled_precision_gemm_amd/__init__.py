@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "null_loop", "decode_nvfp4_f16",
+__all__ = ["Plan", "BsgError", "LibraryNotBuilt", "load_library", "bench_loop", "null_loop", "run_noalloc", "NOALLOC_SCRATCH_BYTES", "decode_nvfp4_f16",
            "FORMATS", "OUT_DTYPES", "SCALE_LAYOUTS", "abi_version", "packed_strides", "Problem", "PROBLEM_V1_SIZE", "PROBLEM_V2_SIZE",
            "pack_scales", "scales_ktile_bytes"]
 
@@ -98,6 +98,7 @@ _SIGNATURES = {
                                       ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_VP), ctypes.c_int,
                                       ctypes.c_int, _VP, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_double)]),
+    "bsg_run_noalloc": (ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP]),
     "bsg_bench_null_loop": (ctypes.c_int, [ctypes.c_int, _VP, ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_double)]),
 }
@@ -218,6 +219,20 @@ class Plan:
 
     def __exit__(self, *exc):
         self.close()
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # BSG_NOALLOC_SCRATCH_BYTES
+
+
+def run_noalloc(fmt: str, M: int, N: int, K: int, A, B, sA, sB, D, alpha: float = 1.0, bias=None, out: str = "bf16",
+                silu: bool = False, device: int = -1, stream=None) -> None:
+    """One GEMM call through bsg_run_noalloc (no allocation; split-K partials in the library's static
+    device scratch).  Packed, single-problem, row-major scales."""
+    prob = Problem(ctypes.sizeof(Problem), FORMATS[fmt], OUT_DTYPES[out],
+                   (EPI_BIAS if bias is not None else 0) | (EPI_SILU if silu else 0), M, N, K, device, 1,
+                   0, 0, 0, 0, 0, 0, 0, 0, 0)
+    _check(load_library().bsg_run_noalloc(ctypes.byref(prob), _ptr(A), _ptr(B), _ptr(sA), _ptr(sB), _ptr(bias),
+                                          float(alpha), _ptr(D), _stream(stream)))
 
 
 def bench_loop(plan: Plan, sets: list[dict], calls_per_set: int, mode: int, stream, with_submit: bool = False):

@@ -168,6 +168,22 @@ bsg_status bsg_run(bsg_plan plan, const void* A, const void* B, const void* sA, 
 bsg_status bsg_run_alpha_ptr(bsg_plan plan, const void* A, const void* B, const void* sA, const void* sB,
                              const float* bias, const float* alpha_dev, void* D, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): one call of the GEMM described by `problem`, with the arguments
+ * and results of bsg_plan_create followed by bsg_run, that allocates nothing -- no device memory, no
+ * host memory.  The plan is built on the stack on every call (the full validation of
+ * bsg_plan_create, so this costs more host time per call than bsg_run on a cached plan).  A problem
+ * whose variant splits K keeps its fp32 partials in a library-owned device array of
+ * BSG_NOALLOC_SCRATCH_BYTES that each GPU holds from its first use by this library until the process
+ * ends; a problem that would need more is refused with BSG_ERR_UNSUPPORTED and nothing is launched
+ * (bsg_plan_create / bsg_run serve it).  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (streams not ordered with each other) race on it and must not be issued.  The
+ * array's device address is looked up on the first call on each device; make that first call
+ * outside graph capture.  Errors: those of bsg_plan_create and bsg_run. */
+#define BSG_NOALLOC_SCRATCH_BYTES (32u << 20)
+bsg_status bsg_run_noalloc(const bsg_problem* problem, const void* A, const void* B, const void* sA, const void* sB,
+                           const float* bias, float alpha, void* D, void* stream);
+
 /* Free a plan.  NULL is accepted.  A plan without workspace is host memory only, and kernels already
  * enqueued with it are unaffected (their arguments were copied at launch).  A plan's workspace is
  * released with hipFree, which waits for the device's outstanding work first. */
