@@ -14,15 +14,15 @@
 // Work split.  A workgroup tile has a "shared" side of 128 or 256 rows and a "private" side of 256
 // rows: with SHARED_A the tile is 128 (M) x 256 (N), otherwise 256 (M) x 128 (N) or, for grids of at
 // least one tile per CU, 256 x 256.  Eight waves (two per SIMD: one wave alone issues VALU work at
-// about half rate and cannot overlap it with its own MFMAs) each compute BS/2 shared x 64 private
-// outputs (BS/64 x 2 accumulators of 32 x 32).
+// about half rate) each compute all 128 shared x 32 private outputs (128-row shared side: 4 x 1
+// accumulators of 32 x 32) or 128 shared x 64 private outputs (256-row shared side: 4 x 2).
 // * The shared operand is decoded once per K tile by all 512 threads (16 or 32 elements each) into a
 //   double-buffered fp16 LDS tile, read by the waves as MFMA fragments.
 // * Each wave decodes its private rows straight into MFMA registers: with the K order inside a
 //   64-element tile permuted so that lane l (r = l % 32, h = l / 32) covers elements 32h .. 32h+31,
 //   one 16-byte chunk per lane per 32-row block holds exactly the four fragments of that block.  The
-//   shared fragments use the same permutation.  (Each private row is decoded by the two waves that
-//   share it.)
+//   shared fragments use the same permutation.  (With the 256-row shared side each private row is
+//   decoded by the two waves that share it.)
 // * Packed bytes and scale codes of K tile k+DIST are copied global -> LDS by buffer_load ... lds
 //   (ring of DIST+1 stages) while tile k is computed and tile k+1's shared rows are decoded; one
 //   barrier per K tile, after each wave has waited for its own copies of tile k+2.  Rows past M / N
@@ -60,26 +60,36 @@ constexpr int COPIES = 4;                    // buffer_load ... lds per wave per
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr float kRescale = 65536.0f;           // 2^16: undoes the 2^-8 of both fp16 operands
 
-// Tile configuration: BS shared rows (128 or 256) x 256 private rows.  Each wave computes BS/2 shared
-// x 64 private outputs (TS x TP accumulators of 32 x 32).
-template <int BS_>
+// Tile configuration: BS shared rows (128 or 256) x 256 private rows, and how the eight waves divide
+// them.  ALL_SHARED: each wave takes all BS shared rows and 32 private rows of its own (TS = BS/32,
+// TP = 1), so every private row is decoded by exactly one wave; otherwise each wave takes half the
+// shared rows and 64 private rows (TS = BS/64, TP = 2), and every private row is decoded by the two
+// waves that share it.  Either way a wave owns TS x TP accumulators of 32 x 32 and issues 16 (BS =
+// 128) or 32 (BS = 256) MFMAs per K tile.  On this route the decode's VALU work adds to the MFMA
+// time rather than hiding under it (measured: ~1870 cycles per K tile for 1024 cycles of MFMA and
+// ~880 of decode VALU per SIMD), so decoding each private row once is worth the shared fragments'
+// extra LDS reads.
+template <int BS_, bool ALL_SHARED_>
 struct Cfg {
   static constexpr int BS = BS_, BP = 256;
+  static constexpr bool ALL_SHARED = ALL_SHARED_;
   static constexpr int ROWS = BS + BP;                   // rows copied per K tile
   static constexpr int RAW_DATA = ROWS * 32;             // packed bytes of a K tile
   static constexpr int RAW_STAGE = RAW_DATA + ROWS * 8;  // + scale codes, 8 bytes per row
   static constexpr int DEC_STAGE = BS * 128;             // decoded shared rows (fp16)
-  static constexpr int LDS_BYTES = NR * RAW_STAGE + 2 * DEC_STAGE;
-  static constexpr int TS = BS / 64, TP = 2;
+  static constexpr int TS = ALL_SHARED ? BS / 32 : BS / 64, TP = ALL_SHARED ? 1 : 2;
+  static constexpr int WSH_ROWS = 32 * TS, WP_ROWS = 32 * TP;  // a wave's shared and private rows
   static constexpr int NSC = BS / 32;                    // shared data copies (32 rows each)
-  static constexpr int EPI_COLS = 32 * TS;               // columns of a wave's block, B shared
   static constexpr int EPI_STRIDE = 32 * (TS > TP ? TS : TP) + 8;  // floats; 4 rows = 32 mod 64 banks
+  static constexpr int MAIN_LDS = NR * RAW_STAGE + 2 * DEC_STAGE;
+  static constexpr int EPI_LDS = WAVES * 32 * EPI_STRIDE * 4;   // epilogue staging, 32 rows per wave
+  static constexpr int LDS_BYTES = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(WAVES * 32 * EPI_STRIDE * 4 <= LDS_BYTES, "epilogue staging");
+  static_assert(EPI_STRIDE % 16 == 8, "two rows 4 apart start 32 banks apart");
   static_assert(BS == 128 || BS == 256, "copy plan");
 };
-using Cfg128 = Cfg<128>;  // 128 x 256 (A shared, small M) or 256 x 128 (B shared)
-using Cfg256 = Cfg<256>;  // 256 x 256, B shared, for grids of at least one tile per CU
+using Cfg128 = Cfg<128, true>;   // 128 x 256 (A shared, small M) or 256 x 128 (B shared)
+using Cfg256 = Cfg<256, false>;  // 256 x 256, B shared, for grids of at least one tile per CU
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -176,9 +186,10 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rp_s = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p_s, (short)0, (int)(ktile ? groups * 4u * (uint32_t)p_all - 4u * (uint32_t)p_first : p_rows * KS), (int)kRsrcWord3);
 
-  // Wave roles: shared half wsh (shared rows BS/2 wsh .. +BS/2), private quarter wp (private rows
-  // 64 wp .. +64); the wave computes those BS/2 x 64 outputs.
-  const int wsh = wave & 1, wp = wave >> 1;
+  // Wave roles: shared rows WSH_ROWS wsh .. +WSH_ROWS and private rows WP_ROWS wp .. +WP_ROWS; the
+  // wave computes those outputs.
+  const int wsh = CF::ALL_SHARED ? 0 : wave & 1, wp = CF::ALL_SHARED ? wave : wave >> 1;
+  constexpr int WSH_ROWS = CF::WSH_ROWS, WP_ROWS = CF::WP_ROWS;
 
   // Copy plan.  A K tile needs ROWS/32 data copies of 32 rows x 32 bytes (lane l: row 32q + l/2,
   // half (l & 1) ^ ((R >> 3) & 1), 16 bytes at 1 KiB * q + 16 l; q < NSC shared, the rest private)
@@ -281,18 +292,18 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     }
   };
 
-  // Fragment addressing.  Private block j: stage row 128 + 64 wp + 32j + r, the lane's half hl.
+  // Fragment addressing.  Private block j: stage row BS + WP_ROWS wp + 32j + r, the lane's half hl.
   const int r32 = lane & 31, hl = lane >> 5;
   uint32_t pf_raw[TP], pf_scale[TP];
 #pragma unroll
   for (int j = 0; j < TP; ++j) {
-    const int R = BS + 64 * wp + 32 * j + r32;
+    const int R = BS + WP_ROWS * wp + 32 * j + r32;
     pf_raw[j] = (uint32_t)(32 * R + 16 * (hl ^ ((R >> 3) & 1)));
     pf_scale[j] = (uint32_t)(RAW_DATA + (SC4 ? 4 * R + 2 * hl : 8 * R + 4 * hl));
   }
-  // Shared block i, slice s: decoded row BS/2 wsh + 32i + r, piece 4 hl + s.
-  const uint32_t sf_row = (uint32_t)(128 * (BS / 2 * wsh + r32));
-  const int sf_sw = (r32 >> 1) & 7;  // (BS/2 wsh + 32i + r) >> 1 & 7 does not depend on wsh, i
+  // Shared block i, slice s: decoded row WSH_ROWS wsh + 32i + r, piece 4 hl + s.
+  const uint32_t sf_row = (uint32_t)(128 * (WSH_ROWS * wsh + r32));
+  const int sf_sw = (r32 >> 1) & 7;  // (WSH_ROWS wsh + 32i + r) >> 1 & 7 does not depend on wsh, i
   uint32_t sf_piece[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) sf_piece[s] = (uint32_t)(((4 * hl + s) ^ sf_sw) << 4);
@@ -380,17 +391,17 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   }
 
   // Epilogue, staged through LDS (free now: the last barrier has passed and no copy is in flight).
-  // The wave's 64 x 64 block -- SHARED_A: rows m0 + 64 wsh + .., columns n0 + 64 wp + ..; otherwise
-  // rows m0 + 64 wp + .., columns n0 + 64 wsh + .. -- goes out in two passes of 32 rows: accumulator
-  // element e of block (i, j) is row 32 mi + 8*(e/4) + 4*hl + e%4, column 32 ni + r32 (mi, ni = i, j
-  // for SHARED_A, else j, i).  Rows are EPI_STRIDE floats apart (4 * 72 = 32 mod 64 banks: the two
-  // rows a store instruction touches land on different banks); each lane then reads 4 consecutive
-  // columns and the wave stores 4 full rows per instruction.
+  // The wave's block -- SHARED_A: rows m0 + WSH_ROWS wsh + .., columns n0 + WP_ROWS wp + ..; otherwise
+  // rows m0 + WP_ROWS wp + .., columns n0 + WSH_ROWS wsh + .. -- goes out in passes of 32 rows:
+  // accumulator element e of block (i, j) is row 32 mi + 8*(e/4) + 4*hl + e%4, column 32 ni + r32
+  // (mi, ni = i, j for SHARED_A, else j, i).  Rows are EPI_STRIDE floats apart (EPI_STRIDE = 8 mod
+  // 16: the two rows a store instruction touches start 32 banks apart); each lane then reads 4
+  // consecutive columns and the wave stores whole rows.
   constexpr int EPI_STRIDE = CF::EPI_STRIDE;
   constexpr int PASSES = SHARED_A ? TS : TP, ECOLS = 32 * (SHARED_A ? TP : TS);
   constexpr int LPR = ECOLS / 4, RPI = 64 / LPR;  // lanes per row (4 columns each), rows per read
   float* stage = (float*)lds + wave * (32 * EPI_STRIDE);
-  const int mw = m0 + (SHARED_A ? BS / 2 * wsh : 64 * wp), nw = n0 + (SHARED_A ? 64 * wp : BS / 2 * wsh);
+  const int mw = m0 + (SHARED_A ? WSH_ROWS * wsh : WP_ROWS * wp), nw = n0 + (SHARED_A ? WP_ROWS * wp : WSH_ROWS * wsh);
   const float alpha = load_alpha(p) * kRescale;
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
