@@ -11,6 +11,7 @@
 #include <stdarg.h>
 #include <stddef.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -40,10 +41,31 @@ namespace {
 
 using bsg::set_error;
 
+// Environment switches, read at plan creation only (never on the per-call path):
+//   BSG_LOG=1              one line per plan on stderr (problem, variant, grid, split factor, workspace);
+//   BSG_LOG=2              also one line per run of such a plan;
+//   BSG_FORCE_ARCH=<name>  the architecture check sees <name> instead of the device's own: any name
+//                          but gfx950 makes plan creation fail with BSG_ERR_DEVICE (a way to exercise
+//                          that path without other hardware); gfx950 leaves the real check in place.
+int env_log_level() {
+  const char* s = getenv("BSG_LOG");
+  return s ? atoi(s) : 0;
+}
+
 // Per-device result of the architecture check, computed once.
 std::mutex g_dev_mutex;
 signed char g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 not
 int g_dev_cus[64];         // compute units of a checked device
+
+// BSG_FORCE_ARCH naming another architecture: refuse before any device query.
+bsg_status check_forced_arch() {
+  const char* forced = getenv("BSG_FORCE_ARCH");
+  if (forced && *forced && strncmp(forced, "gfx950", 6) != 0) {
+    set_error("BSG_FORCE_ARCH=%s: this library is built for gfx950 (MI355X) only", forced);
+    return BSG_ERR_DEVICE;
+  }
+  return BSG_OK;
+}
 
 bsg_status check_device(int dev) {
   int count = 0;
@@ -243,6 +265,7 @@ const char* bsg_status_string(bsg_status s) {
     case BSG_ERR_HIP: return "BSG_ERR_HIP";
     case BSG_ERR_ALLOC: return "BSG_ERR_ALLOC";
     case BSG_ERR_ABI: return "BSG_ERR_ABI";
+    default: break;
   }
   return "BSG_ERR_UNKNOWN";
 }
@@ -264,6 +287,8 @@ bsg_status build_plan(const bsg_problem* problem, bsg_plan_s* plan) {
   if (st != BSG_OK) return st;
   problem = &prob;
   st = validate(problem);
+  if (st != BSG_OK) return st;
+  st = check_forced_arch();
   if (st != BSG_OK) return st;
   int dev = problem->device;
   if (dev < 0) {
@@ -327,6 +352,15 @@ bsg_status build_plan(const bsg_problem* problem, bsg_plan_s* plan) {
   plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n * a.splits), 1, (unsigned)problem->batch)
                              : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, (unsigned)problem->batch);
   plan->block = dim3((unsigned)v.block_threads, 1, 1);
+  plan->log_level = env_log_level();
+  if (plan->log_level >= 1)
+    fprintf(stderr,
+            "bsg: plan %s M=%lld N=%lld K=%lld batch=%lld -> %s tile %dx%dx%d grid (%u,%u,%u) block %u splits %d "
+            "workspace %llu B on device %d\n",
+            problem->format == BSG_FMT_MXFP8 ? "mxfp8" : "nvfp4", (long long)problem->M, (long long)problem->N,
+            (long long)problem->K, (long long)problem->batch, plan->variant, plan->tile_m, plan->tile_n,
+            plan->tile_k, plan->grid.x, plan->grid.y, plan->grid.z, plan->block.x, a.splits,
+            (unsigned long long)plan->workspace_bytes, dev);
   return BSG_OK;
 }
 
@@ -359,6 +393,9 @@ bsg_status launch_plan(const bsg_plan_s* plan, const void* A, const void* B, con
   a.alpha = alpha;
   a.alpha_ptr = alpha_dev;
   a.D = D;
+  if (plan->log_level >= 2)
+    fprintf(stderr, "bsg: run %s A=%p B=%p sA=%p sB=%p bias=%p alpha=%g alpha_dev=%p D=%p stream=%p\n",
+            plan->variant, A, B, sA, sB, (const void*)bias, (double)alpha, (const void*)alpha_dev, D, stream);
   const hipError_t e = plan->launch(a, plan->grid, plan->block, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("kernel launch failed: %s", hipGetErrorString(e));

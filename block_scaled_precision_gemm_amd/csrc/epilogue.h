@@ -46,9 +46,18 @@ __device__ __forceinline__ uint16_t to_out_bits(float y) {
   }
 }
 
+// Two outputs in one dword (lo in bits 0..15).  BF16: one paired conversion (the same round to
+// nearest even as two single ones, without the shift and or that join them).  FP16: single
+// conversions, which the compiler fuses with a preceding multiply or fma into one rounding.
 template <Out O>
 __device__ __forceinline__ uint32_t pack2_out(float lo, float hi) {
-  return (uint32_t)to_out_bits<O>(lo) | ((uint32_t)to_out_bits<O>(hi) << 16);
+  if constexpr (O == Out::BF16) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+  } else {
+    return (uint32_t)to_out_bits<O>(lo) | ((uint32_t)to_out_bits<O>(hi) << 16);
+  }
 }
 
 __device__ __forceinline__ float load_alpha(const GemmArgs& p) {

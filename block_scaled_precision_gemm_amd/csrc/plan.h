@@ -20,6 +20,7 @@ struct bsg_plan_s {
   int tile_m, tile_n, tile_k;
   void* workspace;          // device memory owned by the plan (split-K partials), or null
   uint64_t workspace_bytes; // bytes of split-K partials the variant needs (0: no split)
+  int log_level;            // BSG_LOG at plan creation: 1 logs the plan, 2 also every run
 };
 
 namespace bsg {

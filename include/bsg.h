@@ -81,17 +81,25 @@ typedef enum bsg_status {
   BSG_ERR_DEVICE = 5,      /* no device, or the device is not gfx950 */
   BSG_ERR_HIP = 6,         /* a HIP runtime call failed (message holds hipGetErrorString) */
   BSG_ERR_ALLOC = 7,       /* host allocation of the plan failed */
-  BSG_ERR_ABI = 8          /* struct_size mismatch or bad enum value */
+  BSG_ERR_ABI = 8,         /* struct_size mismatch or bad enum value */
+  /* Not statuses.  These two give each enum of this header the whole int32 range, so that any int a
+   * C caller stores in one (an unknown status code, a bad format) is a value the library may read. */
+  BSG_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  BSG_STATUS_RANGE_MAX_ = 2147483647
 } bsg_status;
 
 typedef enum bsg_format {
   BSG_FMT_MXFP8 = 1, /* E4M3 elements, E8M0 scale per 32 K */
-  BSG_FMT_NVFP4 = 2  /* packed E2M1 elements, E4M3 scale per 16 K, global fp32 alpha */
+  BSG_FMT_NVFP4 = 2, /* packed E2M1 elements, E4M3 scale per 16 K, global fp32 alpha */
+  BSG_FMT_RANGE_MIN_ = -2147483647 - 1,
+  BSG_FMT_RANGE_MAX_ = 2147483647
 } bsg_format;
 
 typedef enum bsg_out_dtype {
   BSG_OUT_BF16 = 1,
-  BSG_OUT_F16 = 2
+  BSG_OUT_F16 = 2,
+  BSG_OUT_RANGE_MIN_ = -2147483647 - 1,
+  BSG_OUT_RANGE_MAX_ = 2147483647
 } bsg_out_dtype;
 
 /* problem flags: epilogue (kEnableBias / kEnableSilu of runNvfp4Gemm) and scale layout */
@@ -151,7 +159,12 @@ typedef struct bsg_plan_info {
 
 /* Validate `problem`, choose the kernel variant for (format, out dtype, epilogue, M bucket) and
  * precompute everything a call needs.  On success *out_plan is a new plan.  Errors: BSG_ERR_NULL,
- * BSG_ERR_ABI, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED, BSG_ERR_DEVICE, BSG_ERR_HIP, BSG_ERR_ALLOC. */
+ * BSG_ERR_ABI, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED, BSG_ERR_DEVICE, BSG_ERR_HIP, BSG_ERR_ALLOC.
+ * Environment, read here (never by bsg_run): BSG_LOG=1 writes one line per plan to stderr (problem,
+ * variant, tile, grid, split factor, workspace); BSG_LOG=2 also one line per run of that plan.
+ * BSG_FORCE_ARCH=<name> makes the architecture check see <name>: any name but gfx950 fails with
+ * BSG_ERR_DEVICE (checked before the device is queried, so it works without a GPU); gfx950 keeps
+ * the check of the real device. */
 bsg_status bsg_plan_create(const bsg_problem* problem, bsg_plan* out_plan);
 
 /* Enqueue D = epi(alpha * A x B^T (+ bias)) on `stream` (a hipStream_t; NULL = the null stream).

@@ -165,6 +165,16 @@ def test_valid_problem_without_gpu_reports_device_error():
     assert b"device" in bsg.load_library().bsg_last_error().lower()
 
 
+def test_forced_architecture_is_refused(monkeypatch):
+    """BSG_FORCE_ARCH=<not gfx950> fails plan creation with BSG_ERR_DEVICE before any device query."""
+    monkeypatch.setenv("BSG_FORCE_ARCH", "gfx942")
+    st, h = _create()
+    assert st == 5 and not h.value
+    assert b"BSG_FORCE_ARCH=gfx942" in bsg.load_library().bsg_last_error()
+    st, _ = _create(K=48)  # validation still comes first
+    assert st == 2
+
+
 def test_null_arguments():
     lib = bsg.load_library()
     assert lib.bsg_plan_create(None, None) == 1

@@ -193,6 +193,22 @@ def test_deterministic_and_alpha_ptr_matches():
     assert np.array_equal(dev["D"].cpu().numpy().view(np.uint16), D0)
 
 
+@pytest.mark.parametrize("fmt,shape,prefix", [
+    ("mxfp8", (4096, 4096, 512), "mxfp8_pp"), ("mxfp8", (128, 4096, 8192), "mxfp8_tiled_128"),
+    ("nvfp4", (128, 2048, 4096), "nvfp4_128x256"), ("nvfp4", (4096, 4096, 256), "nvfp4_256x256")],
+    ids=["mxfp8_pp", "mxfp8_tiled_split", "nvfp4_split", "nvfp4_256x256"])
+def test_every_kernel_family_is_deterministic(fmt, shape, prefix):
+    # the same inputs twice give bit-identical D: no race between LDS stages or split partials
+    p = si.problem(fmt, *shape, seed=610, bias=True, silu=True, out="bf16")
+    plan = make_plan(p)
+    assert plan.info()["variant"].startswith(prefix), plan.info()
+    dev = to_device(p)
+    D0 = run(p, plan=plan, dev=dev)
+    D1 = run(p, plan=plan, dev=dev)
+    assert np.array_equal(D0, D1)
+    plan.close()
+
+
 def test_e8m0_extreme_scales():
     # one nonzero product per entry: A[i, 0] = B[j, 0] = 1.0; sA[i, 0] sweeps every E8M0 code 0..255
     # (0 = 2^-127, 255 = NaN) against sB in {2^-1, 2^0, 2^1}, so products span 2^-128 .. 2^128 (fp32
@@ -271,6 +287,33 @@ def test_plan_info():
     plan = bsg.Plan("mxfp8", 4096, 4096, 4096, out="bf16")
     info = plan.info()
     assert info["workspace_bytes"] == 0 and info["block"] > 0 and info["variant"].startswith("mxfp8")
+
+
+def test_log_levels_and_forced_architecture(monkeypatch, capfd):
+    p = si.problem("nvfp4", 128, 1024, 4096, seed=701)
+    dev = to_device(p)
+    capfd.readouterr()
+    monkeypatch.setenv("BSG_LOG", "2")
+    plan = make_plan(p)  # BSG_LOG is read at plan creation
+    info = plan.info()
+    plan.run(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha=float(p["alpha"]))
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert f"-> {info['variant']} " in err and f"splits {info['grid'][0] // 4}" in err, err
+    assert f"bsg: run {info['variant']} " in err, err
+    monkeypatch.setenv("BSG_LOG", "0")
+    quiet = make_plan(p)
+    quiet.run(dev["A"], dev["B"], dev["sA"], dev["sB"], dev["D"], alpha=float(p["alpha"]))
+    torch.cuda.synchronize()
+    assert "bsg:" not in capfd.readouterr().err
+    monkeypatch.setenv("BSG_FORCE_ARCH", "gfx942")
+    with pytest.raises(bsg.BsgError) as e:
+        make_plan(p)
+    assert e.value.status_name == "BSG_ERR_DEVICE" and "BSG_FORCE_ARCH=gfx942" in str(e.value)
+    monkeypatch.setenv("BSG_FORCE_ARCH", "gfx950")  # the real device is checked, and it is gfx950
+    make_plan(p).close()
+    plan.close()
+    quiet.close()
 
 
 # NVFP4 small-M problems split K across workgroups (fp32 partials in the plan's workspace, summed in
