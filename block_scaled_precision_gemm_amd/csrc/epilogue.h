@@ -60,6 +60,35 @@ __device__ __forceinline__ uint32_t pack2_out(float lo, float hi) {
   }
 }
 
+// f16(a0 * b0 + c0) | f16(a1 * b1 + c1) << 16, each product-sum rounded once from the exact value
+// (v_fma_mixlo_f16, then v_fma_mixhi_f16 writing the high half in place: no shift and or).
+__device__ __forceinline__ uint32_t f16x2_fma_rounded(float a0, float b0, float c0, float a1, float b1, float c1) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3" : "=v"(d) : "v"(a0), "v"(b0), "v"(c0));
+  asm("v_fma_mixhi_f16 %0, %1, %2, %3" : "+v"(d) : "v"(a1), "v"(b1), "v"(c1));
+  return d;
+}
+
+// Two epilogue outputs in one dword (acc0's in bits 0..15).  FP16: the last step of each --
+// alpha * acc + bias, or y * 1/(1 + e^-y) for SiLU -- is one fused multiply-add rounded once to fp16.
+// BF16: epi_value in fp32, then the paired conversion.
+template <bool SILU, Out O>
+__device__ __forceinline__ uint32_t epi_pack2(float acc0, float acc1, float alpha, float bias0, float bias1) {
+  if constexpr (O == Out::F16) {
+    if constexpr (SILU) {
+      constexpr float kLog2e = 1.44269504088896341f;
+      const float y0 = __builtin_fmaf(alpha, acc0, bias0), y1 = __builtin_fmaf(alpha, acc1, bias1);
+      const float r0 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y0 * kLog2e));
+      const float r1 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y1 * kLog2e));
+      return f16x2_fma_rounded(y0, r0, 0.0f, y1, r1, 0.0f);
+    } else {
+      return f16x2_fma_rounded(alpha, acc0, bias0, alpha, acc1, bias1);
+    }
+  } else {
+    return pack2_out<O>(epi_value<SILU, O>(acc0, alpha, bias0), epi_value<SILU, O>(acc1, alpha, bias1));
+  }
+}
+
 __device__ __forceinline__ float load_alpha(const GemmArgs& p) {
   return p.alpha_ptr ? *p.alpha_ptr : p.alpha;
 }

@@ -328,10 +328,8 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const v16f& a = acc[i][j];
-        const uint32_t lo = pack2_out<O>(epi_value<SILU, O>(a[4 * g + 0], alpha, bv[0]),
-                                         epi_value<SILU, O>(a[4 * g + 1], alpha, bv[1]));
-        const uint32_t hi = pack2_out<O>(epi_value<SILU, O>(a[4 * g + 2], alpha, bv[2]),
-                                         epi_value<SILU, O>(a[4 * g + 3], alpha, bv[3]));
+        const uint32_t lo = epi_pack2<SILU, O>(a[4 * g + 0], a[4 * g + 1], alpha, bv[0], bv[1]);
+        const uint32_t hi = epi_pack2<SILU, O>(a[4 * g + 2], a[4 * g + 3], alpha, bv[2], bv[3]);
         *(uint2*)(eb + (32 * i + r) * EPI_ROW + 2 * c0) = make_uint2(lo, hi);
       }
     }

@@ -412,10 +412,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void mxfp8_tiled_kernel(GemmArgs p) 
         if constexpr (SPLIT) {
           *(v4f*)dst = (v4f){a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
         } else {
-          const uint32_t lo = pack2_out<O>(epi_value<SILU, O>(a[4 * g + 0], alpha, bv[j][g][0]),
-                                           epi_value<SILU, O>(a[4 * g + 1], alpha, bv[j][g][1]));
-          const uint32_t hi = pack2_out<O>(epi_value<SILU, O>(a[4 * g + 2], alpha, bv[j][g][2]),
-                                           epi_value<SILU, O>(a[4 * g + 3], alpha, bv[j][g][3]));
+          const uint32_t lo = epi_pack2<SILU, O>(a[4 * g + 0], a[4 * g + 1], alpha, bv[j][g][0], bv[j][g][1]);
+          const uint32_t hi = epi_pack2<SILU, O>(a[4 * g + 2], a[4 * g + 3], alpha, bv[j][g][2], bv[j][g][3]);
           *(uint2*)dst = make_uint2(lo, hi);
         }
       }

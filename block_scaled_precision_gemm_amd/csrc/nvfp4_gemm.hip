@@ -431,8 +431,8 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
         v4f b = {0.f, 0.f, 0.f, 0.f};
         if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
         uint2 o;
-        o.x = pack2_out<O>(epi_value<SILU, O>(v[0], alpha, b[0]), epi_value<SILU, O>(v[1], alpha, b[1]));
-        o.y = pack2_out<O>(epi_value<SILU, O>(v[2], alpha, b[2]), epi_value<SILU, O>(v[3], alpha, b[3]));
+        o.x = epi_pack2<SILU, O>(v[0], v[1], alpha, b[0], b[1]);
+        o.y = epi_pack2<SILU, O>(v[2], v[3], alpha, b[2], b[3]);
         *(uint2*)((uint16_t*)p.D + (size_t)m * p.ldd + n) = o;
       }
     }

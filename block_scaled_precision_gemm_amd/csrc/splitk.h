@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   v4f b = {0.f, 0.f, 0.f, 0.f};
   if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};  // bias: 4-byte aligned
   uint32_t* D = (uint32_t*)((uint16_t*)p.D + (size_t)m * p.ldd + n);
-  D[0] = pack2_out<O>(epi_value<SILU, O>(s[0], alpha, b[0]), epi_value<SILU, O>(s[1], alpha, b[1]));
-  D[1] = pack2_out<O>(epi_value<SILU, O>(s[2], alpha, b[2]), epi_value<SILU, O>(s[3], alpha, b[3]));
+  D[0] = epi_pack2<SILU, O>(s[0], s[1], alpha, b[0], b[1]);
+  D[1] = epi_pack2<SILU, O>(s[2], s[3], alpha, b[2], b[3]);
 }
 
 // Enqueue the finish kernel of a split plan (grid.z of the GEMM launch = batch).
