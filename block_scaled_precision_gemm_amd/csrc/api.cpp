@@ -352,6 +352,10 @@ bsg_status build_plan(const bsg_problem* problem, bsg_plan_s* plan) {
   plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n * a.splits), 1, (unsigned)problem->batch)
                              : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, (unsigned)problem->batch);
   plan->block = dim3((unsigned)v.block_threads, 1, 1);
+  // A persistent kernel takes at most one workgroup per CU; a multiple of 8 keeps each workgroup's
+  // tiles on one XCD (workgroups go to the XCDs round-robin).
+  if (v.persistent && g_dev_cus[dev] > 0 && g_dev_cus[dev] % 8 == 0 && plan->grid.x > (unsigned)g_dev_cus[dev])
+    plan->grid.x = (unsigned)g_dev_cus[dev];
   plan->log_level = env_log_level();
   if (plan->log_level >= 1)
     fprintf(stderr,

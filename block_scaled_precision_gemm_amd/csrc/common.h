@@ -75,6 +75,7 @@ struct KernelVariant {
   // partials per split (stored by the GEMM kernel, read back by the finish kernel), and the fixed
   // cost of splitting at all (the finish kernel's launch and ramp, the split kernel's own prologue).
   float ktile_us = 0.0f, partial_us_per_mib = 0.0f, split_fixed_us = 0.0f;
+  bool persistent = false;  // the kernel loops over tiles: launch at most one workgroup per CU
 };
 
 // Variant tables, one per format: index = out dtype (0 bf16, 1 f16) * 4 + bias * 2 + silu.

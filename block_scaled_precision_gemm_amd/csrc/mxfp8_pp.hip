@@ -29,6 +29,10 @@
 // * XCD-aware tile order: workgroups go to the 8 XCDs round-robin, so each XCD gets a contiguous
 //   range of tile ids, walked in groups of 8 tile-rows; the tiles an XCD runs at once share A and B
 //   panels in its L2.
+// * Persistent: the plan launches at most one workgroup per CU; workgroup b computes the tiles of
+//   virtual ids b, b + grid, b + 2 grid, ... (with a grid that is a multiple of 8 each keeps its
+//   XCD, and every round covers the same tiles as a one-tile-per-workgroup launch), which saves
+//   the workgroup relaunch between tiles.
 //
 // Scaled-MFMA operand layout (measured on the device): lane l (r = l % 32, h = l / 32) holds K bytes
 // [16h, 16h+16) and [32+16h, 32+16h+16) of its row's 64-byte slice; its scale byte is the E8M0
@@ -111,7 +115,10 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave >> 2, ws = wave & 3;
   const int r = lane & 31, h = lane >> 5;
-  const int2 t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n);
+  const int n_tiles = p.tiles_m * p.tiles_n;
+#pragma unroll 1
+  for (int vb = blockIdx.x; vb < n_tiles; vb += gridDim.x) {  // one tile per pass (body not re-indented)
+  const int2 t = tile_of(vb, p.tiles_m, p.tiles_n);
   const int m0 = t.x * BM, n0 = t.y * BN;
   const int K = p.K, KB = K >> 5, KT = K / BK;  // K tiles of 128
   const int m_valid = min(BM, p.M - m0), n_valid = min(BN, p.N - n0);
@@ -345,6 +352,8 @@ __global__ __launch_bounds__(THREADS, 1) void mxfp8_pp_kernel(GemmArgs p) {
     const int m = mw + row, n = nw + cc;
     if (m < p.M && n < p.N) *(v4i*)(D + (size_t)m * p.ldd + n) = v;
   }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // staging read before the next prologue
+  }
 }
 
 template <Out O, bool BIAS, bool SILU>
@@ -356,7 +365,8 @@ hipError_t launch_pp(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t st
 }
 
 #define BSG_MX_PP(O, B, S) \
-  { "mxfp8_pp_256x256x64_w8", &launch_pp<O, B, S>, BM, BN, BK, THREADS, (uint32_t)LDS_BYTES, true }
+  { "mxfp8_pp_256x256x64_w8", &launch_pp<O, B, S>, BM, BN, BK, THREADS, (uint32_t)LDS_BYTES, true, 1, 0.0f, 0.0f, \
+    0.0f, true }
 const KernelVariant kPp[8] = {
     BSG_MX_PP(Out::BF16, false, false), BSG_MX_PP(Out::BF16, false, true),
     BSG_MX_PP(Out::BF16, true, false),  BSG_MX_PP(Out::BF16, true, true),
