@@ -289,6 +289,21 @@ def test_plan_info():
     assert info["workspace_bytes"] == 0 and info["block"] > 0 and info["variant"].startswith("mxfp8")
 
 
+def test_persistent_launch_shape():
+    # the ping-pong kernel loops over tiles: at most one workgroup per CU (a multiple of 8, so each
+    # keeps its XCD); the tiled kernels keep one workgroup per tile
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = bsg.Plan("mxfp8", 8192, 8192, 8192, out="f16", bias=True, silu=True)
+    info = plan.info()
+    assert info["variant"].startswith("mxfp8_pp")
+    assert info["grid"][0] == (min(1024, cus) if cus % 8 == 0 else 1024), (info, cus)
+    small = bsg.Plan("mxfp8", 1024, 1024, 512)  # a tiled plan: one workgroup per tile
+    si_ = small.info()
+    assert not si_["variant"].startswith("mxfp8_pp") and si_["grid"][0] == (1024 // si_["tile"][0]) * (1024 // si_["tile"][1])
+    plan.close()
+    small.close()
+
+
 def test_log_levels_and_forced_architecture(monkeypatch, capfd):
     p = si.problem("nvfp4", 128, 1024, 4096, seed=701)
     dev = to_device(p)
