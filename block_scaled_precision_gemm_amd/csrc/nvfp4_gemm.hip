@@ -25,7 +25,9 @@
 //   decoded by the two waves that share it.)
 // * Packed bytes and scale codes of K tile k+DIST are copied global -> LDS by buffer_load ... lds
 //   (ring of DIST+1 stages) while tile k is computed and tile k+1's shared rows are decoded; one
-//   barrier per K tile, after each wave has waited for its own copies of tile k+2.  Rows past M / N
+//   barrier per K tile, after each wave has waited for its own copies of tile k+2.  Row-major scale
+//   codes come 16 bytes per row for 4 K tiles (K % 256 == 0): every row's codes are a separate
+//   piece of memory, and the copies cost per piece far more than per byte.  Rows past M / N
 //   read as zeros through the buffer range check; the missing half of a final half tile
 //   (K % 64 == 32) decodes with scale code 0, i.e. as zeros.
 // * Split-K for small M x N: the grid holds tiles x S workgroups; split s covers K tiles
@@ -81,7 +83,8 @@ struct Cfg {
   static constexpr int WSH_ROWS = 32 * TS, WP_ROWS = 32 * TP;  // a wave's shared and private rows
   static constexpr int NSC = BS / 32;                    // shared data copies (32 rows each)
   static constexpr int EPI_STRIDE = 32 * (TS > TP ? TS : TP) + 8;  // floats; 4 rows = 32 mod 64 banks
-  static constexpr int MAIN_LDS = NR * RAW_STAGE + 2 * DEC_STAGE;
+  static constexpr int SRING = ROWS * 16;                // scale codes of 4 K tiles, 16 bytes per row
+  static constexpr int MAIN_LDS = NR * RAW_STAGE + 2 * DEC_STAGE + 2 * SRING;
   static constexpr int EPI_LDS = WAVES * 32 * EPI_STRIDE * 4;   // epilogue staging, 32 rows per wave
   static constexpr int LDS_BYTES = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -124,19 +127,26 @@ __device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
   return make_int2(first_m + in_group % gsize, in_group / gsize);
 }
 
-// SC4: scale codes copied 4 bytes per row and K tile (one copy per wave covers 64 rows), for scale
-// rows that are dword-aligned (K-tile-major layout, or row-major with K % 64 == 0); otherwise 2 bytes
-// per row half (two copies per wave).
-template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT, bool SC4>
+// Scale-code copy plan SCM:
+// 2: row-major scales with K % 256 == 0: 16 bytes per row for 4 K tiles (one copy per wave covers 64
+//    rows, issued once per 4 K tiles into a two-slot ring).  Each row's codes are a separate piece of
+//    memory, so the number of pieces copied, not their size, sets the cost: 4 tiles per piece.
+// 1: dword-aligned scale rows otherwise (K-tile-major layout, where one copy reads 256 contiguous
+//    bytes, or row-major with K % 64 == 0): 4 bytes per row and K tile, one copy per wave.
+// 0: 2 bytes per row half (two copies per wave).
+template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT, int SCM>
 __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   select_batch(p);
   constexpr int BS = CF::BS, BP = CF::BP, TS = CF::TS, TP = CF::TP, NSC = CF::NSC;
   constexpr int RAW_DATA = CF::RAW_DATA, RAW_STAGE = CF::RAW_STAGE, DEC_STAGE = CF::DEC_STAGE;
   constexpr int BM = SHARED_A ? BS : BP, BN = SHARED_A ? BP : BS;
-  constexpr int NCOP = SC4 ? COPIES - 1 : COPIES;  // copies per wave per K tile
+  constexpr bool SC4 = SCM >= 1;  // one copy per wave covers 64 rows' codes
+  constexpr int NCOP = SCM == 2 ? COPIES - 2 : SCM == 1 ? COPIES - 1 : COPIES;  // copies per wave per K tile
+  constexpr int SRING = CF::SRING;
   __shared__ __attribute__((aligned(16))) uint8_t lds[CF::LDS_BYTES];
   uint8_t* const raw = lds;
   uint8_t* const dec = lds + NR * RAW_STAGE;
+  uint8_t* const sring = dec + 2 * DEC_STAGE;  // SCM 2: codes of K tiles 4g .. 4g+3 in slot g & 1
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -197,8 +207,9 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // 256 q + 4 l = 8R + 4 (l & 1)).  BS = 256: wave w issues shared copy w and private copy 8 + w.
   // BS = 128: wave w issues copy q2 = w + (w & 4) (shared copies 0..3 for w < 4; for w >= 4 a
   // repeat of its own private copy, which writes the same bytes to the same place) and private copy
-  // 4 + w.  Either way the same four copies in every wave, without branches or selected LDS
-  // addresses (either would make the compiler drain all copies before LDS reads).
+  // 4 + w.  Either way the same copies in every wave, without selected LDS addresses (which would
+  // make the compiler drain all copies before LDS reads).  (SCM 2 instead copies the codes of 4 K
+  // tiles at once, 16 bytes per row, after the data of every fourth tile.)
   const int qp = NSC + wave, qs = NSC == 8 ? wave : wave + (wave & 4);
   const bool has_shared = qs < NSC;
   auto copy_off = [&](int q, bool data, uint32_t& off, int& half) {
@@ -229,16 +240,26 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // Copy offsets are loop-invariant (so the compiler's wait bookkeeping stays exact).  The missing
   // half of a final half tile (K % 64 == 32) is still copied -- the next row's first bytes, or zeros
   // past the range for the last row -- and the decode gives it scale code 0, i.e. zero elements.
-  // Ring positions count from the split's first tile, so that the steady-state loop, unrolled by the
-  // ring size, sees every stage and decoded-buffer offset as a constant (immediate LDS offsets).
-  static_assert((NR & (NR - 1)) == 0, "ring size a power of two");
-  auto ring = [&](int kt) -> uint32_t { return (uint32_t)(kt - kb) & (NR - 1); };
-  auto copy_tile = [&](int kt) {
+  // Ring positions are K tile numbers mod NR; the steady-state loop starts at a multiple of NR, so that,
+  // unrolled by the ring size, it sees every stage and decoded-buffer offset as a constant (immediate
+  // LDS offsets).
+  static_assert((NR & (NR - 1)) == 0 && NR == 4, "ring size a power of two; SCM 2 groups 4 K tiles");
+  auto ring = [&](int kt) -> uint32_t { return (uint32_t)kt & (NR - 1); };
+  // SCM 2: the codes of K tiles 4g .. 4g+3 (16 bytes per row at byte 16 g of the row; past K: other
+  // rows' codes or zeros, never used), into slot g & 1.
+  auto copy_scales = [&](int g) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r4_s, (lds_void*)(sring + (g & 1) * SRING + 1024 * c4), 16, o_s4, (uint32_t)g * 16u, 0, 0);
+  };
+  // SCALES (SCM 2): also the scale group that starts at K tile kt, issued after the tile's data.
+  auto copy_tile = [&](int kt, bool scales) {
+    const int kq = kt;
     kt = min(kt, ke - 1);  // past the last tile re-read it (never consumed): uniform load counts
     uint8_t* st = raw + ring(kt) * RAW_STAGE;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_q, (lds_void*)(st + 1024 * qs), 16, o_sd, (uint32_t)kt * 32u, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rp_q, (lds_void*)(st + 1024 * qp), 16, o_pd, (uint32_t)kt * 32u, 0, 0);
-    if constexpr (SC4) {
+    if constexpr (SCM == 2) {
+      if (scales) copy_scales(kq >> 2);
+    } else if constexpr (SC4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r4_s, (lds_void*)(st + RAW_DATA + 256 * c4), 4, o_s4, (uint32_t)kt * ktb4, 0, 0);
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r2_s, (lds_void*)(st + RAW_DATA + 256 * qs), 2, o_ss, (uint32_t)kt * ktb2, 0, 0);
@@ -262,9 +283,19 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   const int sd_row = BS == 256 ? tid >> 1 : tid >> 2;
   const int sd_h = BS == 256 ? tid & 1 : (tid >> 1) & 1, sd_sub = BS == 256 ? 0 : tid & 1;
   const uint32_t sd_raw = (uint32_t)(32 * sd_row + 16 * (sd_h ^ ((sd_row >> 3) & 1)));
-  // the two codes of row R, half h: a zero-extended 4-byte slot at 8R + 4h, or (SC4) bytes 2h, 2h+1
-  // of the row's 4-byte slot at 4R, read as 2 bytes: the same value either way
-  const uint32_t sd_scale = (uint32_t)(RAW_DATA + (SC4 ? 4 * sd_row + 2 * sd_h : 8 * sd_row + 4 * sd_h));
+  // The two codes of row R, half h of K tile kt: SCM 0: a zero-extended 4-byte slot at 8R + 4h of the
+  // tile's raw stage; SCM 1: bytes 2h, 2h+1 of the row's 4-byte slot at 4R (read as 2 bytes: the same
+  // value); SCM 2: bytes 4 (kt % 4) + 2h, +1 of the row's 16 bytes in the scale ring.  row_off: the
+  // part that does not depend on kt.
+  auto scale_row_off = [&](int R, int h) -> uint32_t {
+    if constexpr (SCM == 2) return (uint32_t)(16 * R + 2 * h);
+    return (uint32_t)(RAW_DATA + (SC4 ? 4 * R + 2 * h : 8 * R + 4 * h));
+  };
+  auto scale_at = [&](int kt, uint32_t row_off) -> const uint8_t* {
+    if constexpr (SCM == 2) return sring + ((kt >> 2) & 1) * SRING + row_off + 4 * (kt & 3);
+    return raw + ring(kt) * RAW_STAGE + row_off;
+  };
+  const uint32_t sd_scale = scale_row_off(sd_row, sd_h);
   auto scale_pair = [&](const uint8_t* at) -> uint32_t {
     if constexpr (SC4) return (uint32_t)*(const uint16_t*)at;
     return *(const uint32_t*)at;
@@ -277,7 +308,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     const uint8_t* st = raw + ring(kt) * RAW_STAGE;
     uint8_t* out = dec + (ring(kt) & 1) * DEC_STAGE;
     const v4i q4 = *(const v4i*)(st + sd_raw);  // the row's half
-    const uint32_t codes = half_scales(scale_pair(st + sd_scale), kt, sd_h, check);
+    const uint32_t codes = half_scales(scale_pair(scale_at(kt, sd_scale)), kt, sd_h, check);
     if constexpr (BS == 256) {
       v4i r[4];
       e2m1x32_scaled_f16(q4, codes, r);
@@ -299,7 +330,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   for (int j = 0; j < TP; ++j) {
     const int R = BS + WP_ROWS * wp + 32 * j + r32;
     pf_raw[j] = (uint32_t)(32 * R + 16 * (hl ^ ((R >> 3) & 1)));
-    pf_scale[j] = (uint32_t)(RAW_DATA + (SC4 ? 4 * R + 2 * hl : 8 * R + 4 * hl));
+    pf_scale[j] = scale_row_off(R, hl);
   }
   // Shared block i, slice s: decoded row WSH_ROWS wsh + 32i + r, piece 4 hl + s.
   const uint32_t sf_row = (uint32_t)(128 * (WSH_ROWS * wsh + r32));
@@ -324,7 +355,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TP; ++j) {
       pq[j] = *(const v4i*)(st + pf_raw[j]);
-      const uint32_t s = e4m3x2_scale_f16x2(half_scales(scale_pair(st + pf_scale[j]), kt, hl, check));
+      const uint32_t s = e4m3x2_scale_f16x2(half_scales(scale_pair(scale_at(kt, pf_scale[j])), kt, hl, check));
       ps[j][0] = f16x2_splat_lo(s);
       ps[j][1] = f16x2_splat_hi(s);
     }
@@ -353,35 +384,59 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     }
   };
 
-  // Prologue: copies of tiles kb .. kb+DIST-1 (clamped); tile kb's shared rows decoded.
+  // Copy waits: at most N + 1 of the wave's copies in flight when EXTRA (a scale group issued after
+  // the data copies the wait leaves in flight), else N.
+  auto wait_copies_x = [&](auto n, bool extra) {
+    constexpr int N = decltype(n)::value;
+    if constexpr (SCM == 2) {
+      if (extra) {
+        wait_copies<N + 1>();
+        return;
+      }
+    }
+    wait_copies<N>();
+  };
+  using IC0 = std::integral_constant<int, 0>;
+  using ICN = std::integral_constant<int, NCOP>;
+  auto starts_group = [&](int kt) { return SCM == 2 && (kt & 3) == 0; };
+
+  // Prologue: copies of tiles kb .. kb+DIST-1 (clamped), with the scale group of tile kb first (SCM
+  // 2) and any group that starts at kb+1 .. kb+DIST-1; tile kb's shared rows decoded.
+  static_assert(DIST == 3, "prologue waits");
+  if constexpr (SCM == 2) copy_scales(kb >> 2);
 #pragma unroll
-  for (int i = 0; i < DIST; ++i) copy_tile(kb + i);
-  wait_copies<(DIST - 1) * NCOP>();
+  for (int i = 0; i < DIST; ++i) copy_tile(kb + i, i > 0 && starts_group(kb + i));
+  // tile kb (and its codes) landed: tiles kb+1, kb+2 and their groups may stay in flight
+  wait_copies_x(std::integral_constant<int, 2 * NCOP>{}, starts_group(kb + 1) || starts_group(kb + 2));
   lds_barrier();  // every wave's copies of tile kb have landed
   decode_shared(kb, Checked{});
-  wait_copies<(DIST - 2) * NCOP>();
+  wait_copies_x(ICN{}, starts_group(kb + 2));
   lds_barrier();  // tile kb decoded, tile kb+1 landed
   // Steady state: step kt issues tile kt+DIST's copies, computes tile kt and decodes tile kt+1's
-  // shared rows; before the barrier that ends it, the wave's copies of tile kt+2 must have landed
-  // (tiles kt+3 .. kt+DIST may stay in flight).  Raw stages in use: kt .. kt+DIST: NR = DIST + 1.
+  // shared rows; before the barrier that ends it, the wave's copies of tile kt+2 (and its scale
+  // group) must have landed: tile kt+3's copies, and its group if it starts one, may stay in flight.
+  // Raw stages in use: kt .. kt+DIST: NR = DIST + 1.
+  auto single = [&](int kt) {
+    copy_tile(kt + DIST, starts_group(kt + DIST));
+    step(kt, Unchecked{});
+    wait_copies_x(ICN{}, starts_group(kt + DIST));
+    lds_barrier();
+  };
   int kt = kb;
+#pragma unroll 1
+  for (; (kt & (NR - 1)) != 0 && kt + DIST < ke; ++kt) single(kt);  // up to a multiple of NR
 #pragma unroll 1
   for (; kt + NR - 1 + DIST < ke; kt += NR) {
 #pragma unroll
-    for (int c = 0; c < NR; ++c) {
-      copy_tile(kt + c + DIST);
+    for (int c = 0; c < NR; ++c) {  // kt + c == c (mod NR)
+      copy_tile(kt + c + DIST, SCM == 2 && ((c + DIST) & 3) == 0);
       step(kt + c, Unchecked{});
-      wait_copies<(DIST - 2) * NCOP>();
+      wait_copies_x(ICN{}, SCM == 2 && ((c + DIST) & 3) == 0);
       lds_barrier();
     }
   }
 #pragma unroll 1
-  for (; kt + DIST < ke; ++kt) {
-    copy_tile(kt + DIST);
-    step(kt, Unchecked{});
-    wait_copies<(DIST - 2) * NCOP>();
-    lds_barrier();
-  }
+  for (; kt + DIST < ke; ++kt) single(kt);
   // Last DIST tiles: nothing left to copy.  Leaves no copy in flight past the end of the kernel.
 #pragma unroll 1
   for (; kt < ke; ++kt) {
@@ -389,6 +444,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
     wait_copies<0>();
     lds_barrier();
   }
+  (void)IC0{};
 
   // Epilogue, staged through LDS (free now: the last barrier has passed and no copy is in flight).
   // The wave's block -- SHARED_A: rows m0 + WSH_ROWS wsh + .., columns n0 + WP_ROWS wp + ..; otherwise
@@ -443,14 +499,17 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU>
 hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
-  const bool sc4 = args.scale_ktile || args.K % 64 == 0;  // scale rows dword-aligned
-  if (args.splits <= 1)
-    return hipLaunchKernel(sc4 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, false, true>
-                               : (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, false, false>,
-                           grid, block, kargs, 0, stream);
-  hipError_t e = hipLaunchKernel(sc4 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, true, true>
-                                     : (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, true, false>,
-                                 grid, block, kargs, 0, stream);
+  // scale copy plan (see nvfp4_kernel): 16-byte row pieces for row-major codes with K % 256 == 0,
+  // 4-byte pieces for other dword-aligned rows, else 2-byte pieces
+  const int scm = !args.scale_ktile && args.K % 256 == 0 ? 2 : (args.scale_ktile || args.K % 64 == 0) ? 1 : 0;
+  auto pick = [&](auto split) -> const void* {
+    constexpr bool SP = decltype(split)::value;
+    return scm == 2 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 2>
+         : scm == 1 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 1>
+                    : (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 0>;
+  };
+  if (args.splits <= 1) return hipLaunchKernel(pick(std::false_type{}), grid, block, kargs, 0, stream);
+  hipError_t e = hipLaunchKernel(pick(std::true_type{}), grid, block, kargs, 0, stream);
   if (e != hipSuccess) return e;
   return launch_splitk_finish<O, BIAS, SILU, 16>(args, grid.z, stream);  // accumulators carry 2^-16
 }
