@@ -152,8 +152,19 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn, split = 0;
   if constexpr (SPLIT) {
-    split = (int)blockIdx.x % p.splits;
-    const int t = (int)blockIdx.x / p.splits;
+    // With a multiple of 8 tiles every split of tile t runs on XCD t % 8 (ids go to the XCDs
+    // round-robin), and the finish kernel's blocks for tile t run there too (splitk.h).  Otherwise
+    // consecutive ids take consecutive splits.
+    const int T = p.tiles_m * p.tiles_n, b = (int)blockIdx.x;
+    int t;
+    if ((T & 7) == 0) {
+      const int r = b >> 3;
+      split = r % p.splits;
+      t = (b & 7) + 8 * (r / p.splits);
+    } else {
+      split = b % p.splits;
+      t = b / p.splits;
+    }
     tm = t / p.tiles_n;
     tn = t - tm * p.tiles_n;
   } else {
@@ -511,7 +522,10 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
   if (args.splits <= 1) return hipLaunchKernel(pick(std::false_type{}), grid, block, kargs, 0, stream);
   hipError_t e = hipLaunchKernel(pick(std::true_type{}), grid, block, kargs, 0, stream);
   if (e != hipSuccess) return e;
-  return launch_splitk_finish<O, BIAS, SILU, 16>(args, grid.z, stream);  // accumulators carry 2^-16
+  // accumulators carry 2^-16; with a multiple of 8 tiles the finish kernel follows the GEMM's XCDs
+  constexpr int TBM = SHARED_A ? CF::BS : CF::BP, TBN = SHARED_A ? CF::BP : CF::BS;
+  if ((args.tiles_m * args.tiles_n) % 8 == 0) return launch_splitk_finish<O, BIAS, SILU, 16, TBM, TBN>(args, grid.z, stream);
+  return launch_splitk_finish<O, BIAS, SILU, 16>(args, grid.z, stream);
 }
 
 #define BSG_NVR(CF, SA, NAME, O, B, S, MAXS)                                                          \

@@ -12,6 +12,12 @@
 // trip) is smaller than latency x bandwidth (~4 MiB: 0.8 us at ~5 TB/s), where a plane-by-plane
 // pass waits on latency; from there on the plane-by-plane order streams at least as fast (measured:
 // 1-2 MiB planes 5-11% faster with LOAD_ALL, 4 MiB planes 1% slower).
+//
+// TBM x TBN (0 x 0: rows in order): the GEMM kernel put every split of tile t on XCD t % 8
+// (workgroups go to the 8 XCDs round-robin by id), and block b sums part of a tile t with
+// t % 8 == b % 8, i.e. on the XCD that wrote those partials.  Measured with the NVFP4 split kernels
+// (256x4096x4096: 6-12% faster per call than splits and finish blocks spread over all XCDs);
+// plain instead of streaming partial stores and loads were slower either way.
 #pragma once
 
 #include "common.h"
@@ -22,29 +28,44 @@ namespace bsg {
 // The largest split factor of any split-capable kernel (KernelVariant::max_splits).
 constexpr int kMaxFinishSplits = 16;
 
-template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, bool LOAD_ALL>
+template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, bool LOAD_ALL, int TBM = 0, int TBN = 0>
 __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   select_batch(p);
-  const int nq = p.N >> 2;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)p.M * nq) return;
-  const int m = (int)(idx / nq), n = (int)(idx - (int64_t)m * nq) * 4;
+  constexpr bool AFFINE = TBM > 0;
+  int m, n;
+  if constexpr (AFFINE) {
+    constexpr int BPT = TBM * TBN / 4 / 256, TPR = TBN / 4;  // blocks per tile, threads per tile row
+    static_assert(BPT * 256 * 4 == TBM * TBN && TBN % 4 == 0, "whole blocks per tile");
+    const int b = (int)blockIdx.x, k = b >> 3;
+    const int t = (b & 7) + 8 * (k / BPT), ti = (k % BPT) * 256 + (int)threadIdx.x;
+    const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
+    m = tm * TBM + ti / TPR;
+    n = tn * TBN + (ti % TPR) * 4;
+    if (m >= p.M || n >= p.N) return;  // ragged tiles (N % 16 == 0: 4 columns all in or all out)
+  } else {
+    const int nq = p.N >> 2;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)p.M * nq) return;
+    m = (int)(idx / nq);
+    n = (int)(idx - (int64_t)m * nq) * 4;
+  }
   const size_t plane = (size_t)p.M * p.N;
   const float* src = p.ws + (size_t)m * p.N + n;
   // streaming loads: every partial is read exactly once; sums in split order either way
+  auto ld = [&](int k) -> v4f { return __builtin_nontemporal_load((const v4f*)(src + k * plane)); };
   v4f s;
   if constexpr (LOAD_ALL) {
     v4f part[kMaxFinishSplits];
 #pragma unroll
     for (int k = 0; k < kMaxFinishSplits; ++k)
-      if (k < p.splits) part[k] = __builtin_nontemporal_load((const v4f*)(src + k * plane));
+      if (k < p.splits) part[k] = ld(k);
     s = part[0];
 #pragma unroll
     for (int k = 1; k < kMaxFinishSplits; ++k)
       if (k < p.splits) s += part[k];
   } else {
-    s = __builtin_nontemporal_load((const v4f*)src);
-    for (int k = 1; k < p.splits; ++k) s += __builtin_nontemporal_load((const v4f*)(src + k * plane));
+    s = ld(0);
+    for (int k = 1; k < p.splits; ++k) s += ld(k);
   }
   const float alpha = load_alpha(p) * (float)(1u << RESCALE_LOG2);
   v4f b = {0.f, 0.f, 0.f, 0.f};
@@ -54,13 +75,20 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   D[1] = epi_pack2<SILU, O>(s[2], s[3], alpha, b[2], b[3]);
 }
 
-// Enqueue the finish kernel of a split plan (grid.z of the GEMM launch = batch).
-template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2>
+// Enqueue the finish kernel of a split plan (grid.z of the GEMM launch = batch).  TBM x TBN > 0: the
+// GEMM kept each tile's splits on one XCD (tiles a multiple of 8, tiles of TBM x TBN).
+template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, int TBM = 0, int TBN = 0>
 hipError_t launch_splitk_finish(const GemmArgs& args, unsigned batch, hipStream_t stream) {
   if (args.splits < 1 || args.splits > kMaxFinishSplits) return hipErrorInvalidValue;
   void* kargs[] = {(void*)&args};
   const int64_t threads = (int64_t)args.M * (args.N >> 2);
   const bool load_all = 16.0 * (double)threads * (double)batch < 4.0 * 1024 * 1024;  // one plane < 4 MiB
+  if constexpr (TBM > 0) {
+    const unsigned blocks = (unsigned)(args.tiles_m * args.tiles_n) * (unsigned)(TBM * TBN / 4 / 256);
+    const void* k = load_all ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, true, TBM, TBN>
+                             : (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, false, TBM, TBN>;
+    return hipLaunchKernel(k, dim3(blocks, 1, batch), dim3(256), kargs, 0, stream);
+  }
   const void* k = load_all ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, true>
                            : (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, false>;
   return hipLaunchKernel(k, dim3((unsigned)((threads + 255) / 256), 1, batch), dim3(256), kargs, 0, stream);
