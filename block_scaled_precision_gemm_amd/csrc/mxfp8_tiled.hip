@@ -92,6 +92,11 @@ __device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
   return make_int2(first_m + in_group % gsize, in_group / gsize);
 }
 
+// The same order for the split-K finish kernel's blocks (splitk.h).
+struct TiledOrder {
+  __device__ static int2 of(int t, int tiles_m, int tiles_n) { return tile_of(t, tiles_m, tiles_n); }
+};
+
 // Copy plan for one operand tile (ROWS rows x 128 bytes): wave w issues COPIES instructions; its
 // instruction q fills LDS rows 8*(COPIES*w + q) .. +8 (1 KiB).  Lane j of an instruction writes LDS
 // bytes [16j, 16j+16) of that KiB: row R = 8*(COPIES*w+q) + j/8, physical chunk j%8, which holds
@@ -473,6 +478,10 @@ hipError_t launch_tiled(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t
   const void* k = three ? tiled_kernel_for<Small3, O, BIAS, SILU>(sm, split) : tiled_kernel_for<C, O, BIAS, SILU>(sm, split);
   const hipError_t e = hipLaunchKernel(k, grid, block, kargs, 0, stream);
   if (e != hipSuccess || !split) return e;
+  // split-major ids with a multiple of 8 tiles put every split of a tile on one XCD (id % 8 is the
+  // same for all of them): the finish kernel's blocks follow (splitk.h)
+  if ((args.tiles_m * args.tiles_n) % 8 == 0)
+    return launch_splitk_finish<O, BIAS, SILU, 0, C::BM, C::BN, TiledOrder>(args, grid.z, stream);
   return launch_splitk_finish<O, BIAS, SILU, 0>(args, grid.z, stream);
 }
 

@@ -15,7 +15,8 @@
 //
 // TBM x TBN (0 x 0: rows in order): the GEMM kernel put every split of tile t on XCD t % 8
 // (workgroups go to the 8 XCDs round-robin by id), and block b sums part of a tile t with
-// t % 8 == b % 8, i.e. on the XCD that wrote those partials.  Measured with the NVFP4 split kernels
+// t % 8 == b % 8, i.e. on the XCD that wrote those partials; TileMap turns t into the tile's
+// (row, column) as the GEMM kernel numbered it.  Measured with the NVFP4 split kernels
 // (256x4096x4096: 6-12% faster per call than splits and finish blocks spread over all XCDs);
 // plain instead of streaming partial stores and loads were slower either way.
 #pragma once
@@ -28,7 +29,16 @@ namespace bsg {
 // The largest split factor of any split-capable kernel (KernelVariant::max_splits).
 constexpr int kMaxFinishSplits = 16;
 
-template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, bool LOAD_ALL, int TBM = 0, int TBN = 0>
+// Tile t of a row-major tile grid.
+struct RowMajorTiles {
+  __device__ static int2 of(int t, int /*tiles_m*/, int tiles_n) {
+    const int tm = t / tiles_n;
+    return make_int2(tm, t - tm * tiles_n);
+  }
+};
+
+template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, bool LOAD_ALL, int TBM = 0, int TBN = 0,
+          class TileMap = RowMajorTiles>
 __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   select_batch(p);
   constexpr bool AFFINE = TBM > 0;
@@ -38,9 +48,9 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
     static_assert(BPT * 256 * 4 == TBM * TBN && TBN % 4 == 0, "whole blocks per tile");
     const int b = (int)blockIdx.x, k = b >> 3;
     const int t = (b & 7) + 8 * (k / BPT), ti = (k % BPT) * 256 + (int)threadIdx.x;
-    const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
-    m = tm * TBM + ti / TPR;
-    n = tn * TBN + (ti % TPR) * 4;
+    const int2 tt = TileMap::of(t, p.tiles_m, p.tiles_n);
+    m = tt.x * TBM + ti / TPR;
+    n = tt.y * TBN + (ti % TPR) * 4;
     if (m >= p.M || n >= p.N) return;  // ragged tiles (N % 16 == 0: 4 columns all in or all out)
   } else {
     const int nq = p.N >> 2;
@@ -77,7 +87,7 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
 
 // Enqueue the finish kernel of a split plan (grid.z of the GEMM launch = batch).  TBM x TBN > 0: the
 // GEMM kept each tile's splits on one XCD (tiles a multiple of 8, tiles of TBM x TBN).
-template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, int TBM = 0, int TBN = 0>
+template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, int TBM = 0, int TBN = 0, class TileMap = RowMajorTiles>
 hipError_t launch_splitk_finish(const GemmArgs& args, unsigned batch, hipStream_t stream) {
   if (args.splits < 1 || args.splits > kMaxFinishSplits) return hipErrorInvalidValue;
   void* kargs[] = {(void*)&args};
@@ -85,8 +95,8 @@ hipError_t launch_splitk_finish(const GemmArgs& args, unsigned batch, hipStream_
   const bool load_all = 16.0 * (double)threads * (double)batch < 4.0 * 1024 * 1024;  // one plane < 4 MiB
   if constexpr (TBM > 0) {
     const unsigned blocks = (unsigned)(args.tiles_m * args.tiles_n) * (unsigned)(TBM * TBN / 4 / 256);
-    const void* k = load_all ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, true, TBM, TBN>
-                             : (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, false, TBM, TBN>;
+    const void* k = load_all ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, true, TBM, TBN, TileMap>
+                             : (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, false, TBM, TBN, TileMap>;
     return hipLaunchKernel(k, dim3(blocks, 1, batch), dim3(256), kargs, 0, stream);
   }
   const void* k = load_all ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, true>
