@@ -507,14 +507,373 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   }
 }
 
+// Warp-specialised variant of the 128-row-shared-side kernel, for row-major scale codes with
+// K % 256 == 0.  Waves 4..7 move data: they copy every row global -> LDS two K tiles at a time (64
+// bytes per row and copy: half the row pieces of single-tile copies) and decode the 128 shared rows
+// of the next K tile into a double-buffered fp16 tile.  Waves 0..3 (one per SIMD) compute: wave w
+// owns all 128 shared rows and private rows 64w .. 64w+63 (4 x 2 accumulators), reads the shared
+// fragments from the decoded tile and decodes its own private rows from the packed bytes into MFMA
+// operands, as nvfp4_kernel does.  Against eight waves that each take all shared rows and 32
+// private rows, the LDS carries about a third less per K tile (each shared fragment is read by 4
+// waves, not 8), which is what bounds these kernels; each private row is still decoded once.
+namespace wsk {
+constexpr int BS = 128, BP = 256, ROWS = BS + BP;
+constexpr int PAIR = ROWS * 64;                      // packed bytes of a K-tile pair (24 KiB)
+constexpr int NP = 4;                                // pair stages
+constexpr int SRING = ROWS * 16;                     // scale codes of 4 K tiles
+constexpr int DEC = BS * 128;                        // a decoded K tile of the shared rows
+constexpr int TS = 4, TP = 2;                        // a compute wave's 32 x 32 blocks
+constexpr int EPI_STRIDE = 32 * TS + 8;              // floats; as nvfp4_kernel's staging
+constexpr int MAIN_LDS = NP * PAIR + 2 * SRING + 2 * DEC;
+constexpr int EPI_LDS = 4 * 32 * EPI_STRIDE * 4;
+constexpr int LDS_BYTES = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+}  // namespace wsk
+
+template <bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT>
+__global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
+  select_batch(p);
+  using namespace wsk;
+  constexpr int BM = SHARED_A ? BS : BP, BN = SHARED_A ? BP : BS;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  uint8_t* const raw = lds;                  // pair P in stage P & 3
+  uint8_t* const sring = lds + NP * PAIR;    // scale group g in slot g & 1
+  uint8_t* const dec = sring + 2 * SRING;    // shared rows of K tile t in buffer t & 1
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn, split = 0;
+  if constexpr (SPLIT) {  // as nvfp4_kernel: a tile's splits on one XCD when the tiles are a multiple of 8
+    const int T = p.tiles_m * p.tiles_n, b = (int)blockIdx.x;
+    int t;
+    if ((T & 7) == 0) {
+      const int r = b >> 3;
+      split = r % p.splits;
+      t = (b & 7) + 8 * (r / p.splits);
+    } else {
+      split = b % p.splits;
+      t = b / p.splits;
+    }
+    tm = t / p.tiles_n;
+    tn = t - tm * p.tiles_n;
+  } else {
+    const int2 t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n);
+    tm = t.x;
+    tn = t.y;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  // K % 256 == 0: K tiles come in scale groups of 4, and a split takes whole groups (at least one:
+  // the host never splits K into more parts than it has groups)
+  const int K = p.K, KG = K / (4 * BK);
+  const int kb = SPLIT ? 4 * (int)((int64_t)split * KG / p.splits) : 0;
+  const int ke = SPLIT ? 4 * (int)((int64_t)(split + 1) * KG / p.splits) : 4 * KG;
+  const uint32_t KH = (uint32_t)K >> 1, KS = (uint32_t)K >> 4;
+  const int r32 = lane & 31, hl = lane >> 5;
+  // Packed bytes of K tile t, row R (0 .. 383, shared rows first), half h: 16 bytes at
+  // 64R + 16 ((2 (t & 1) + h) ^ ((R >> 2) & 3)) of pair stage (t >> 1) & 3 (the swizzle puts the 16
+  // rows that 16 consecutive lanes read on distinct banks); its two scale codes at 16R + 4 (t & 3) +
+  // 2h of scale slot (t >> 2) & 1.
+  auto raw_at = [&](int kt, int R, int h) -> const uint8_t* {
+    return raw + ((kt >> 1) & (NP - 1)) * PAIR + 64 * R + 16 * ((2 * (kt & 1) + h) ^ ((R >> 2) & 3));
+  };
+  auto codes_at = [&](int kt, int R, int h) -> const uint8_t* {
+    return sring + ((kt >> 2) & 1) * SRING + 16 * R + 4 * (kt & 3) + 2 * h;
+  };
+
+  if (wave >= 4) {
+    // ---- data waves: copies and the shared rows' decode ------------------------------------------
+    const int pw = wave - 4;
+    const uint32_t s_pitch = (uint32_t)(SHARED_A ? p.row_a : p.row_b), p_pitch = (uint32_t)(SHARED_A ? p.row_b : p.row_a);
+    const uint8_t* s_q = SHARED_A ? p.A + (size_t)m0 * s_pitch : p.B + (size_t)n0 * s_pitch;
+    const uint8_t* p_q = SHARED_A ? p.B + (size_t)n0 * p_pitch : p.A + (size_t)m0 * p_pitch;
+    const int s_first = SHARED_A ? m0 : n0, p_first = SHARED_A ? n0 : m0;
+    const uint8_t* s_s = (SHARED_A ? p.sA : p.sB) + (size_t)s_first * KS;
+    const uint8_t* p_s = (SHARED_A ? p.sB : p.sA) + (size_t)p_first * KS;
+    const int s_rows = SHARED_A ? min(BS, p.M - m0) : min(BS, p.N - n0);
+    const int p_rows = SHARED_A ? min(BP, p.N - n0) : min(BP, p.M - m0);
+    const __amdgpu_buffer_rsrc_t rs_q =
+        __builtin_amdgcn_make_buffer_rsrc((void*)s_q, (short)0, (int)((s_rows - 1) * s_pitch + KH), (int)kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rp_q =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p_q, (short)0, (int)((p_rows - 1) * p_pitch + KH), (int)kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)s_s, (short)0, (int)(s_rows * KS), (int)kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rp_s = __builtin_amdgcn_make_buffer_rsrc((void*)p_s, (short)0, (int)(p_rows * KS), (int)kRsrcWord3);
+
+    // Pair P: 24 copies of 16 rows x 64 bytes (copy q: rows 16q + l/4, lane l's 16-byte piece
+    // j = l & 3 at byte 64R + 16j, holding the row's piece j ^ ((R >> 2) & 3) of the pair); data wave
+    // pw issues copies 6pw .. 6pw+5.  Scale codes of K tiles 4g .. 4g+3: copy c (of 6) moves rows
+    // 64c .. 64c+63, 16 bytes each; data wave pw issues c = pw and c = pw + 4 (waves 2, 3 repeat
+    // c = pw: same bytes, same place).  Rows past M / N read as zeros (outside the buffer ranges).
+    // (Offsets computed at each use: an offset array used from these lambdas made the host
+    // compilation drop the launch stub.)
+    auto copy_pair = [&](int P) {
+      uint8_t* st = raw + (P & (NP - 1)) * PAIR;
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        const int q = 6 * pw + u, R = 16 * q + (lane >> 2);
+        const bool sh = q < BS / 16;  // wave-uniform
+        const uint32_t off = (uint32_t)(sh ? R : R - BS) * (sh ? s_pitch : p_pitch) + 16u * (uint32_t)((lane & 3) ^ ((R >> 2) & 3));
+        const __amdgpu_buffer_rsrc_t rq = sh ? rs_q : rp_q;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(st + 1024 * q), 16, off, (uint32_t)P * 64u, 0, 0);
+      }
+    };
+    auto copy_scales = [&](int g) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int c4 = c == 0 ? pw : (pw < 2 ? pw + 4 : pw);
+        const bool sh = 64 * c4 < BS;
+        const uint32_t off = (uint32_t)(64 * c4 + lane - (sh ? 0 : BS)) * KS;
+        const __amdgpu_buffer_rsrc_t rq = sh ? rs_s : rp_s;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sring + (g & 1) * SRING + 1024 * c4), 16, off, (uint32_t)g * 16u, 0, 0);
+      }
+    };
+    // Shared decode of K tile t into buffer t & 1: lane l takes shared row 32pw + (l & 31), half
+    // l >> 5, and stores its 32 fp16 values as pieces 4h .. 4h+3 of the row at position
+    // piece ^ ((R >> 1) & 7).
+    const int sd_row = 32 * pw + r32;
+    auto decode_shared = [&](int kt) {
+      const v4i q4 = *(const v4i*)raw_at(kt, sd_row, hl);
+      const uint32_t codes = (uint32_t)*(const uint16_t*)codes_at(kt, sd_row, hl);
+      v4i r[4];
+      e2m1x32_scaled_f16(q4, codes, r);
+      uint8_t* out = dec + (kt & 1) * DEC + 128 * sd_row;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) *(v4i*)(out + (((4 * hl + d) ^ ((sd_row >> 1) & 7)) << 4)) = r[d];
+    };
+    // Schedule (kb, ke multiples of 4).  Step t decodes the shared rows of tile t + 1; the compute
+    // waves read the packed private rows of tile t (and, ahead, t + 1).  Step 4q copies scale group
+    // q + 1 and then pair 2q + 3, step 4q + 2 pair 2q + 4: a pair's stage was last read at the step
+    // before, the group's slot (group q - 1) too.  Before the barrier ending step t, tile t + 2 (its
+    // pair and group) must have landed: at steps 4q and 4q + 1 the last 14 of the wave's copies may
+    // stay in flight (pair 2q + 2, group q + 1, pair 2q + 3), at steps 4q + 2 and 4q + 3 the last 12
+    // (pairs 2q + 3, 2q + 4); near the split's end, where copies past it are skipped, none.
+    auto step = [&](int kt, auto cc) {
+      constexpr int C = decltype(cc)::value;  // kt & 3
+      const bool full = (kt & ~3) + 8 < ke;   // every copy the counted waits assume was issued
+      if constexpr (C == 0) {
+        if (kt + 4 < ke) {
+          copy_scales((kt >> 2) + 1);
+          copy_pair((kt >> 1) + 3);
+        }
+      } else if constexpr (C == 2) {
+        if (kt + 6 < ke) copy_pair((kt >> 1) + 3);
+      }
+      if (kt + 1 < ke) decode_shared(kt + 1);
+      if (!full)
+        wait_copies<0>();
+      else if constexpr (C < 2)
+        wait_copies<14>();
+      else
+        wait_copies<12>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // as lds_barrier's lgkmcnt(0), seen by the compiler's wait
+      lds_barrier();                       // bookkeeping
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    // Prologue: the copies the schedule would have issued before step kb -- pair kb/2, scale group
+    // kb/4, pairs kb/2 + 1 and kb/2 + 2 (past a 4-tile split's end: bytes never used) -- then tile kb
+    // (pair kb/2, group kb/4) landed and decoded.
+    copy_pair(kb >> 1);
+    copy_scales(kb >> 2);
+    copy_pair((kb >> 1) + 1);
+    copy_pair((kb >> 1) + 2);
+    wait_copies<12>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();  // (1) pair kb/2 and group kb/4 visible
+    decode_shared(kb);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();  // (2) tile kb's shared rows decoded
+#pragma unroll 1
+    for (int kt = kb; kt < ke; kt += 4) {
+      step(kt, C0{});
+      step(kt + 1, C1{});
+      step(kt + 2, C2{});
+      step(kt + 3, C3{});
+    }
+    return;  // the epilogue is the compute waves'
+  }
+
+  // ---- compute waves ----------------------------------------------------------------------------
+  v16f acc[TS][TP];
+#pragma unroll
+  for (int i = 0; i < TS; ++i)
+#pragma unroll
+    for (int j = 0; j < TP; ++j) acc[i][j] = v16f{};
+  // Shared block i, slice s: decoded row 32i + r, piece (4 hl + s) ^ ((r >> 1) & 7).  Private block j:
+  // row BS + 64 wave + 32j + r, the lane's half hl, decoded slice by slice in registers.
+  const int sw = (r32 >> 1) & 7;
+  uint32_t piece[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) piece[s] = (uint32_t)(((4 * hl + s) ^ sw) << 4);
+  const uint32_t sf_row = (uint32_t)(128 * r32);
+  // Packed private rows of tile t in register set t & 1 (read a step ahead).
+  v4i pq0[TP], pq1[TP];
+  uint32_t pc0[TP], pc1[TP];
+  auto read_private = [&](int kt, v4i* pq, uint32_t* pc) {
+#pragma unroll
+    for (int j = 0; j < TP; ++j) {
+      const int R = BS + 64 * wave + 32 * j + r32;
+      pq[j] = *(const v4i*)raw_at(kt, R, hl);
+      pc[j] = (uint32_t)*(const uint16_t*)codes_at(kt, R, hl);
+    }
+  };
+  // Scale codes of a tile as fp16 pairs, in register set t & 1 like its packed rows.
+  uint32_t ps0[TP][2], ps1[TP][2];
+  auto prep_scales = [&](const uint32_t* pc, uint32_t (*ps)[2]) {
+#pragma unroll
+    for (int j = 0; j < TP; ++j) {
+      const uint32_t s2 = e4m3x2_scale_f16x2(pc[j]);
+      ps[j][0] = f16x2_splat_lo(s2);
+      ps[j][1] = f16x2_splat_hi(s2);
+    }
+  };
+  v4i sf[2][TS], pf[2][TP];
+  auto load_shared = [&](int kt, int s, v4i* f) {
+    const uint8_t* d = dec + (kt & 1) * DEC + sf_row;
+#pragma unroll
+    for (int i = 0; i < TS; ++i) f[i] = *(const v4i*)(d + 32 * 128 * i + piece[s]);
+  };
+  auto decode_private = [&](const v4i* pq, uint32_t (*ps)[2], int s, v4i* f) {
+#pragma unroll
+    for (int j = 0; j < TP; ++j) f[j] = e2m1x8_scaled_f16x8((uint32_t)pq[j][s], ps[j][s >> 1]);
+  };
+  auto mfmas = [&](const v4i* a, const v4i* b) {
+#pragma unroll
+    for (int i = 0; i < TS; ++i)
+#pragma unroll
+      for (int j = 0; j < TP; ++j)
+        acc[i][j] = SHARED_A ? mfma_f16(a[i], b[j], acc[i][j]) : mfma_f16(b[j], a[i], acc[i][j]);
+  };
+  // Scheduling groups for one slice: an MFMA, the LDS reads (whose data is needed a slice later),
+  // then the remaining MFMAs with the VALU work spread between them.
+  auto slice_groups = [](auto nreads, auto nvalu) {
+    constexpr int NRD = decltype(nreads)::value, NV = decltype(nvalu)::value;
+    constexpr int PER = (NV + TS * TP - 2) / (TS * TP - 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+    for (int m = 1; m < TS * TP; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+  // One K tile.  On entry sf[0] and pf[0] hold slice 0's fragments and set t & 1 the tile's packed
+  // private rows and scales.  Slice s's MFMAs run while slice s + 1's shared fragments are read and
+  // its private ones decoded; the tile t + 1 packed private rows are read during slice 0 (visible
+  // since the previous barrier) and their scales prepared during slice 2.  The barrier that ends
+  // the step comes before slice 3's MFMAs, which hide the next tile's first shared reads and
+  // private decode.  At the split's last tile those reads fetch bytes that are never used.
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+  using I28 = std::integral_constant<int, 28>;
+  auto compute = [&](int kt, auto par) {
+    constexpr int P = decltype(par)::value;  // kt & 1
+    const v4i* pq = P ? pq1 : pq0;
+    uint32_t (*ps)[2] = P ? ps1 : ps0;
+    v4i* pqn = P ? pq0 : pq1;
+    uint32_t* pcn = P ? pc0 : pc1;
+    uint32_t (*psn)[2] = P ? ps0 : ps1;
+    // slice 0
+    mfmas(sf[0], pf[0]);
+    load_shared(kt, 1, sf[1]);
+    read_private(kt + 1, pqn, pcn);
+    decode_private(pq, ps, 1, pf[1]);
+    slice_groups(I8{}, I16{});
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 1
+    mfmas(sf[1], pf[1]);
+    load_shared(kt, 2, sf[0]);
+    decode_private(pq, ps, 2, pf[0]);
+    slice_groups(I4{}, I16{});
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 2
+    mfmas(sf[0], pf[0]);
+    load_shared(kt, 3, sf[1]);
+    decode_private(pq, ps, 3, pf[1]);
+    prep_scales(pcn, psn);
+    slice_groups(I4{}, I28{});
+    __builtin_amdgcn_sched_barrier(0);
+    // tile kt's reads done; tile kt + 1's shared rows decoded (the data waves' step kt ends here)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();
+    // slice 3, with the next tile's slice 0 fragments
+    mfmas(sf[1], pf[1]);
+    load_shared(kt + 1, 0, sf[0]);
+    decode_private(pqn, psn, 0, pf[0]);
+    slice_groups(I4{}, I16{});
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  lds_barrier();  // (1)
+  read_private(kb, pq0, pc0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  lds_barrier();  // (2): tile kb's shared rows decoded
+  load_shared(kb, 0, sf[0]);
+  prep_scales(pc0, ps0);
+  decode_private(pq0, ps0, 0, pf[0]);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+#pragma unroll 1
+  for (int kt = kb; kt < ke; kt += 2) {  // ke - kb is a multiple of 4
+    compute(kt, P0{});
+    compute(kt + 1, P1{});
+  }
+
+  // Epilogue (as nvfp4_kernel's, TS x TP blocks): SHARED_A: rows m0 + .., columns n0 + 64 wave + ..;
+  // otherwise rows m0 + 64 wave + .., columns n0 + ...
+  constexpr int PASSES = SHARED_A ? TS : TP, ECOLS = 32 * (SHARED_A ? TP : TS);
+  constexpr int LPR = ECOLS / 4, RPI = 64 / LPR;
+  float* stage = (float*)lds + wave * (32 * EPI_STRIDE);
+  const int mw = m0 + (SHARED_A ? 0 : 64 * wave), nw = n0 + (SHARED_A ? 64 * wave : 0);
+  const float alpha = load_alpha(p) * kRescale;
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+#pragma unroll
+    for (int i = 0; i < TS; ++i)
+#pragma unroll
+      for (int j = 0; j < TP; ++j) {
+        const int mi = SHARED_A ? i : j, ni = SHARED_A ? j : i;
+        if (mi != pass) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          stage[(8 * (e >> 2) + 4 * hl + (e & 3)) * EPI_STRIDE + 32 * ni + r32] = acc[i][j][e];
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c4 = 4 * (lane % LPR);
+    const int n = nw + c4;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int row = RPI * it + lane / LPR;
+      const int m = mw + 32 * pass + row;
+      const v4f v = *(const v4f*)(stage + row * EPI_STRIDE + c4);
+      if (m >= p.M || n >= p.N) continue;  // N % 16 == 0: a lane's 4 columns are all in or all out
+      if constexpr (SPLIT) {
+        __builtin_nontemporal_store(v, (v4f*)(p.ws + (size_t)split * p.M * p.N + (size_t)m * p.N + n));
+      } else {
+        v4f b = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
+        uint2 o;
+        o.x = epi_pack2<SILU, O>(v[0], v[1], alpha, b[0], b[1]);
+        o.y = epi_pack2<SILU, O>(v[2], v[3], alpha, b[2], b[3]);
+        *(uint2*)((uint16_t*)p.D + (size_t)m * p.ldd + n) = o;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass overwrites
+  }
+}
+
 template <class CF, bool SHARED_A, Out O, bool BIAS, bool SILU>
 hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t stream) {
   void* kargs[] = {(void*)&args};
   // scale copy plan (see nvfp4_kernel): 16-byte row pieces for row-major codes with K % 256 == 0,
   // 4-byte pieces for other dword-aligned rows, else 2-byte pieces
   const int scm = !args.scale_ktile && args.K % 256 == 0 ? 2 : (args.scale_ktile || args.K % 64 == 0) ? 1 : 0;
+  const bool ws = CF::BS == 128 && scm == 2;  // warp-specialised kernel
   auto pick = [&](auto split) -> const void* {
     constexpr bool SP = decltype(split)::value;
+    if constexpr (CF::BS == 128)
+      if (ws) return (const void*)&nvfp4_ws_kernel<SHARED_A, O, BIAS, SILU, SP>;
     return scm == 2 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 2>
          : scm == 1 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 1>
                     : (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 0>;
