@@ -507,8 +507,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   }
 }
 
-// Warp-specialised variant of the 128-row-shared-side kernel, for row-major scale codes with
-// K % 256 == 0.  Waves 4..7 move data: they copy every row global -> LDS two K tiles at a time (64
+// Warp-specialised variant of the 128-row-shared-side kernel, for K % 256 == 0 (either scale layout).  Waves 4..7 move data: they copy every row global -> LDS two K tiles at a time (64
 // bytes per row and copy: half the row pieces of single-tile copies) and decode the 128 shared rows
 // of the next K tile into a double-buffered fp16 tile.  Waves 0..3 (one per SIMD) compute: wave w
 // owns all 128 shared rows and private rows 64w .. 64w+63 (4 x 2 accumulators), reads the shared
@@ -530,7 +529,7 @@ constexpr int LDS_BYTES = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 }  // namespace wsk
 
-template <bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT>
+template <bool SHARED_A, Out O, bool BIAS, bool SILU, bool SPLIT, bool KTILE>
 __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   select_batch(p);
   using namespace wsk;
@@ -571,13 +570,18 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   const int r32 = lane & 31, hl = lane >> 5;
   // Packed bytes of K tile t, row R (0 .. 383, shared rows first), half h: 16 bytes at
   // 64R + 16 ((2 (t & 1) + h) ^ ((R >> 2) & 3)) of pair stage (t >> 1) & 3 (the swizzle puts the 16
-  // rows that 16 consecutive lanes read on distinct banks); its two scale codes at 16R + 4 (t & 3) +
-  // 2h of scale slot (t >> 2) & 1.
+  // rows that 16 consecutive lanes read on distinct banks).  Its two scale codes, in scale slot
+  // (t >> 2) & 1: row-major codes at 16R + 4 (t & 3) + 2h (a row's 16 codes of the 4-tile group);
+  // K-tile-major codes as the layout has them, [tile][row] -- private rows' 1 KiB per K tile at
+  // 1024 (t & 3), shared rows' 512 bytes at 4096 + 512 (t & 3), 4 bytes per row.
   auto raw_at = [&](int kt, int R, int h) -> const uint8_t* {
     return raw + ((kt >> 1) & (NP - 1)) * PAIR + 64 * R + 16 * ((2 * (kt & 1) + h) ^ ((R >> 2) & 3));
   };
   auto codes_at = [&](int kt, int R, int h) -> const uint8_t* {
-    return sring + ((kt >> 2) & 1) * SRING + 16 * R + 4 * (kt & 3) + 2 * h;
+    const uint8_t* slot = sring + ((kt >> 2) & 1) * SRING;
+    if constexpr (KTILE)
+      return slot + (R < BS ? 4096 + 512 * (kt & 3) + 4 * R : 1024 * (kt & 3) + 4 * (R - BS)) + 2 * h;
+    return slot + 16 * R + 4 * (kt & 3) + 2 * h;
   };
 
   if (wave >= 4) {
@@ -587,16 +591,24 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
     const uint8_t* s_q = SHARED_A ? p.A + (size_t)m0 * s_pitch : p.B + (size_t)n0 * s_pitch;
     const uint8_t* p_q = SHARED_A ? p.B + (size_t)n0 * p_pitch : p.A + (size_t)m0 * p_pitch;
     const int s_first = SHARED_A ? m0 : n0, p_first = SHARED_A ? n0 : m0;
-    const uint8_t* s_s = (SHARED_A ? p.sA : p.sB) + (size_t)s_first * KS;
-    const uint8_t* p_s = (SHARED_A ? p.sB : p.sA) + (size_t)p_first * KS;
+    // Scale codes: row-major [rows][KS], or K-tile-major (the 4 codes of K tile t of row r at
+    // (t * rows + r) * 4; the range then ends at the array's end, and rows past the operand's last
+    // row read other rows' codes, which only reach outputs that are never stored).
+    const int s_all = SHARED_A ? p.M : p.N, p_all = SHARED_A ? p.N : p.M;  // operand rows
+    const uint32_t s_rowb = KTILE ? 4u : KS, p_rowb = KTILE ? 4u : KS;
+    const uint8_t* s_s = (SHARED_A ? p.sA : p.sB) + (size_t)s_first * s_rowb;
+    const uint8_t* p_s = (SHARED_A ? p.sB : p.sA) + (size_t)p_first * p_rowb;
     const int s_rows = SHARED_A ? min(BS, p.M - m0) : min(BS, p.N - n0);
     const int p_rows = SHARED_A ? min(BP, p.N - n0) : min(BP, p.M - m0);
     const __amdgpu_buffer_rsrc_t rs_q =
         __builtin_amdgcn_make_buffer_rsrc((void*)s_q, (short)0, (int)((s_rows - 1) * s_pitch + KH), (int)kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rp_q =
         __builtin_amdgcn_make_buffer_rsrc((void*)p_q, (short)0, (int)((p_rows - 1) * p_pitch + KH), (int)kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)s_s, (short)0, (int)(s_rows * KS), (int)kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rp_s = __builtin_amdgcn_make_buffer_rsrc((void*)p_s, (short)0, (int)(p_rows * KS), (int)kRsrcWord3);
+    const uint32_t ktiles = KS >> 2;  // K tiles of 64: one 4-byte K-tile-major entry per row each
+    const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)s_s, (short)0, (int)(KTILE ? ktiles * 4u * (uint32_t)s_all - 4u * (uint32_t)s_first : s_rows * KS), (int)kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rp_s = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p_s, (short)0, (int)(KTILE ? ktiles * 4u * (uint32_t)p_all - 4u * (uint32_t)p_first : p_rows * KS), (int)kRsrcWord3);
 
     // Pair P: 24 copies of 16 rows x 64 bytes (copy q: rows 16q + l/4, lane l's 16-byte piece
     // j = l & 3 at byte 64R + 16j, holding the row's piece j ^ ((R >> 2) & 3) of the pair); data wave
@@ -616,14 +628,26 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(st + 1024 * q), 16, off, (uint32_t)P * 64u, 0, 0);
       }
     };
+    // K-tile-major codes of group g: copy c < 4 moves the private rows' 1 KiB of K tile 4g + c
+    // (lane l: rows 4l .. 4l+3), copy 4 + c' the shared rows' 512 bytes of K tiles 4g + 2c' and
+    // 4g + 2c' + 1 (lanes 0..31 and 32..63), each into its place in the slot.
     auto copy_scales = [&](int g) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int c4 = c == 0 ? pw : (pw < 2 ? pw + 4 : pw);
-        const bool sh = 64 * c4 < BS;
-        const uint32_t off = (uint32_t)(64 * c4 + lane - (sh ? 0 : BS)) * KS;
-        const __amdgpu_buffer_rsrc_t rq = sh ? rs_s : rp_s;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sring + (g & 1) * SRING + 1024 * c4), 16, off, (uint32_t)g * 16u, 0, 0);
+        if constexpr (KTILE) {
+          const bool sh = c4 >= 4;  // wave-uniform
+          const uint32_t off = sh ? (uint32_t)(2 * (c4 - 4) + (lane >> 5)) * 4u * (uint32_t)s_all + 16u * (uint32_t)(lane & 31)
+                                  : (uint32_t)c4 * 4u * (uint32_t)p_all + 16u * (uint32_t)lane;
+          const __amdgpu_buffer_rsrc_t rq = sh ? rs_s : rp_s;
+          const uint32_t gofs = (uint32_t)g * 16u * (uint32_t)(sh ? s_all : p_all);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sring + (g & 1) * SRING + 1024 * c4), 16, off, gofs, 0, 0);
+        } else {
+          const bool sh = 64 * c4 < BS;
+          const uint32_t off = (uint32_t)(64 * c4 + lane - (sh ? 0 : BS)) * KS;
+          const __amdgpu_buffer_rsrc_t rq = sh ? rs_s : rp_s;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sring + (g & 1) * SRING + 1024 * c4), 16, off, (uint32_t)g * 16u, 0, 0);
+        }
       }
     };
     // Shared decode of K tile t into buffer t & 1: lane l takes shared row 32pw + (l & 31), half
@@ -869,11 +893,13 @@ hipError_t launch(const GemmArgs& args, dim3 grid, dim3 block, hipStream_t strea
   // scale copy plan (see nvfp4_kernel): 16-byte row pieces for row-major codes with K % 256 == 0,
   // 4-byte pieces for other dword-aligned rows, else 2-byte pieces
   const int scm = !args.scale_ktile && args.K % 256 == 0 ? 2 : (args.scale_ktile || args.K % 64 == 0) ? 1 : 0;
-  const bool ws = CF::BS == 128 && scm == 2;  // warp-specialised kernel
+  const bool ws = CF::BS == 128 && args.K % 256 == 0;  // warp-specialised kernel, either scale layout
   auto pick = [&](auto split) -> const void* {
     constexpr bool SP = decltype(split)::value;
     if constexpr (CF::BS == 128)
-      if (ws) return (const void*)&nvfp4_ws_kernel<SHARED_A, O, BIAS, SILU, SP>;
+      if (ws)
+        return args.scale_ktile ? (const void*)&nvfp4_ws_kernel<SHARED_A, O, BIAS, SILU, SP, true>
+                                : (const void*)&nvfp4_ws_kernel<SHARED_A, O, BIAS, SILU, SP, false>;
     return scm == 2 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 2>
          : scm == 1 ? (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 1>
                     : (const void*)&nvfp4_kernel<CF, SHARED_A, O, BIAS, SILU, SP, 0>;

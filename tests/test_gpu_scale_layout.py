@@ -53,6 +53,8 @@ KTILE_SHAPES = [
     ("nvfp4", (128, 1024, 4096)),   # shared A, split
     ("nvfp4", (300, 2048, 1056)),   # 256 x 128 tiles (shared B), ragged M, half K tile
     ("nvfp4", (640, 4096, 256)),    # shared B, unsplit
+    ("nvfp4", (200, 1040, 1280)),   # shared B, ragged M and N, split into whole 4-tile scale groups
+    ("nvfp4", (96, 2048, 4864)),    # shared A, ragged M, split (19 scale groups over the splits)
     ("nvfp4", (4096, 4096, 288)),   # 256 x 256 tiles, a final half K tile
 ]
 
