@@ -38,6 +38,15 @@ __device__ __forceinline__ uint32_t e4m3x2_scale_f16x2(uint32_t sc) {
   return t | nan | (y & 0x80008000u);
 }
 
+// The same for the code pair a byte-permute selector picks from a dword of four codes: sel =
+// 0x010C000C takes bytes 0, 1 (as e4m3x2_scale_f16x2), 0x030C020C bytes 2, 3.
+__device__ __forceinline__ uint32_t e4m3x2_scale_f16x2_sel(uint32_t w, uint32_t sel) {
+  const uint32_t y = __builtin_amdgcn_perm(0u, w, sel);
+  const uint32_t t = (y >> 1) & 0x3F803F80u;
+  const uint32_t nan = (t + 0x00800080u) & 0x40004000u;
+  return t | nan | (y & 0x80008000u);
+}
+
 // fp16 pair (x.lo, x.lo) and (x.hi, x.hi) of a dword of two fp16.
 __device__ __forceinline__ uint32_t f16x2_splat_lo(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x01000100u); }
 __device__ __forceinline__ uint32_t f16x2_splat_hi(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x03020302u); }

@@ -570,19 +570,35 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   const int r32 = lane & 31, hl = lane >> 5;
   // Packed bytes of K tile t, row R (0 .. 383, shared rows first), half h: 16 bytes at
   // 64R + 16 ((2 (t & 1) + h) ^ ((R >> 2) & 3)) of pair stage (t >> 1) & 3 (the swizzle puts the 16
-  // rows that 16 consecutive lanes read on distinct banks).  Its two scale codes, in scale slot
-  // (t >> 2) & 1: row-major codes at 16R + 4 (t & 3) + 2h (a row's 16 codes of the 4-tile group);
-  // K-tile-major codes as the layout has them, [tile][row] -- private rows' 1 KiB per K tile at
-  // 1024 (t & 3), shared rows' 512 bytes at 4096 + 512 (t & 3), 4 bytes per row.
+  // rows that 16 consecutive lanes read on distinct banks).  Scale codes, in scale slot (t >> 2) & 1:
+  // row-major codes at 16R (a row's 16 codes of the 4-tile group, read whole: 16 lanes' 16-byte
+  // reads of 16 rows are one pass over the banks, where 2-byte reads of 32 rows 16 bytes apart
+  // collide four ways), K-tile-major codes as the layout has them, [tile][row] -- private rows'
+  // 1 KiB per K tile at 1024 (t & 3), shared rows' 512 bytes at 4096 + 512 (t & 3), 4 bytes per row.
+  // Either way a tile's four codes of a row are one dword ("code word"); half h's two are bytes 2h,
+  // 2h + 1 of it, picked by a byte permute.
   auto raw_at = [&](int kt, int R, int h) -> const uint8_t* {
     return raw + ((kt >> 1) & (NP - 1)) * PAIR + 64 * R + 16 * ((2 * (kt & 1) + h) ^ ((R >> 2) & 3));
   };
-  auto codes_at = [&](int kt, int R, int h) -> const uint8_t* {
+  using CodeRead = std::conditional_t<KTILE, uint32_t, v4i>;  // what one read of a row's codes gets
+  auto read_codes = [&](int kt, int R) -> CodeRead {
     const uint8_t* slot = sring + ((kt >> 2) & 1) * SRING;
     if constexpr (KTILE)
-      return slot + (R < BS ? 4096 + 512 * (kt & 3) + 4 * R : 1024 * (kt & 3) + 4 * (R - BS)) + 2 * h;
-    return slot + 16 * R + 4 * (kt & 3) + 2 * h;
+      return *(const uint32_t*)(slot + (R < BS ? 4096 + 512 * (kt & 3) + 4 * R : 1024 * (kt & 3) + 4 * (R - BS)));
+    else
+      return *(const v4i*)(slot + 16 * R);
   };
+  auto code_word = [](const CodeRead& c, auto tq) -> uint32_t {  // tq: the tile's index in its group
+    if constexpr (KTILE)
+      return c;
+    else
+      return (uint32_t)c[decltype(tq)::value];
+  };
+  const uint32_t code_sel = hl ? 0x030C020Cu : 0x010C000Cu;  // this lane's half's two codes
+  // Decoded shared rows: 16-byte piece j of row R at 128R + ((j ^ f(R)) << 4), f(R) = (R & 7) ^
+  // ((R >> 3) & 1): 16 lanes reading piece j of 16 consecutive rows (256 bytes per pass) and 8
+  // lanes storing into 8 consecutive rows (128 bytes per pass) both touch distinct banks.
+  auto dec_swz = [](int R) { return (R & 7) ^ ((R >> 3) & 1); };
 
   if (wave >= 4) {
     // ---- data waves: copies and the shared rows' decode ------------------------------------------
@@ -651,17 +667,20 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
       }
     };
     // Shared decode of K tile t into buffer t & 1: lane l takes shared row 32pw + (l & 31), half
-    // l >> 5, and stores its 32 fp16 values as pieces 4h .. 4h+3 of the row at position
-    // piece ^ ((R >> 1) & 7).
-    const int sd_row = 32 * pw + r32;
-    auto decode_shared = [&](int kt) {
+    // l >> 5, and stores its 32 fp16 values as pieces 4h .. 4h+3 of the row.  tq: t & 3.
+    const int sd_row = 32 * pw + r32, sd_swz = dec_swz(sd_row);
+    auto decode_shared = [&](int kt, auto tq) {
       const v4i q4 = *(const v4i*)raw_at(kt, sd_row, hl);
-      const uint32_t codes = (uint32_t)*(const uint16_t*)codes_at(kt, sd_row, hl);
+      const uint32_t s = e4m3x2_scale_f16x2_sel(code_word(read_codes(kt, sd_row), tq), code_sel);
+      const uint32_t s0 = f16x2_splat_lo(s), s1 = f16x2_splat_hi(s);
       v4i r[4];
-      e2m1x32_scaled_f16(q4, codes, r);
+      r[0] = e2m1x8_scaled_f16x8((uint32_t)q4[0], s0);
+      r[1] = e2m1x8_scaled_f16x8((uint32_t)q4[1], s0);
+      r[2] = e2m1x8_scaled_f16x8((uint32_t)q4[2], s1);
+      r[3] = e2m1x8_scaled_f16x8((uint32_t)q4[3], s1);
       uint8_t* out = dec + (kt & 1) * DEC + 128 * sd_row;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) *(v4i*)(out + (((4 * hl + d) ^ ((sd_row >> 1) & 7)) << 4)) = r[d];
+      for (int d = 0; d < 4; ++d) *(v4i*)(out + (((4 * hl + d) ^ sd_swz) << 4)) = r[d];
     };
     // Schedule (kb, ke multiples of 4).  Step t decodes the shared rows of tile t + 1; the compute
     // waves read the packed private rows of tile t (and, ahead, t + 1).  Step 4q copies scale group
@@ -681,7 +700,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
       } else if constexpr (C == 2) {
         if (kt + 6 < ke) copy_pair((kt >> 1) + 3);
       }
-      if (kt + 1 < ke) decode_shared(kt + 1);
+      if (kt + 1 < ke) decode_shared(kt + 1, std::integral_constant<int, (C + 1) & 3>{});
       if (!full)
         wait_copies<0>();
       else if constexpr (C < 2)
@@ -705,7 +724,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
     wait_copies<12>();
     __builtin_amdgcn_s_waitcnt(0xC07F);
     lds_barrier();  // (1) pair kb/2 and group kb/4 visible
-    decode_shared(kb);
+    decode_shared(kb, std::integral_constant<int, 0>{});
     __builtin_amdgcn_s_waitcnt(0xC07F);
     lds_barrier();  // (2) tile kb's shared rows decoded
 #pragma unroll 1
@@ -724,30 +743,30 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   for (int i = 0; i < TS; ++i)
 #pragma unroll
     for (int j = 0; j < TP; ++j) acc[i][j] = v16f{};
-  // Shared block i, slice s: decoded row 32i + r, piece (4 hl + s) ^ ((r >> 1) & 7).  Private block j:
-  // row BS + 64 wave + 32j + r, the lane's half hl, decoded slice by slice in registers.
-  const int sw = (r32 >> 1) & 7;
+  // Shared block i, slice s: decoded row 32i + r, piece (4 hl + s) ^ f(r) (f(32i + r) = f(r)).  Private
+  // block j: row BS + 64 wave + 32j + r, the lane's half hl, decoded slice by slice in registers.
+  const int sw = dec_swz(r32);
   uint32_t piece[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) piece[s] = (uint32_t)(((4 * hl + s) ^ sw) << 4);
   const uint32_t sf_row = (uint32_t)(128 * r32);
   // Packed private rows of tile t in register set t & 1 (read a step ahead).
   v4i pq0[TP], pq1[TP];
-  uint32_t pc0[TP], pc1[TP];
-  auto read_private = [&](int kt, v4i* pq, uint32_t* pc) {
+  CodeRead pc0[TP], pc1[TP];
+  auto read_private = [&](int kt, v4i* pq, CodeRead* pc) {
 #pragma unroll
     for (int j = 0; j < TP; ++j) {
       const int R = BS + 64 * wave + 32 * j + r32;
       pq[j] = *(const v4i*)raw_at(kt, R, hl);
-      pc[j] = (uint32_t)*(const uint16_t*)codes_at(kt, R, hl);
+      pc[j] = read_codes(kt, R);
     }
   };
-  // Scale codes of a tile as fp16 pairs, in register set t & 1 like its packed rows.
+  // Scale codes of a tile as fp16 pairs, in register set t & 1 like its packed rows.  tq: t & 3.
   uint32_t ps0[TP][2], ps1[TP][2];
-  auto prep_scales = [&](const uint32_t* pc, uint32_t (*ps)[2]) {
+  auto prep_scales = [&](const CodeRead* pc, uint32_t (*ps)[2], auto tq) {
 #pragma unroll
     for (int j = 0; j < TP; ++j) {
-      const uint32_t s2 = e4m3x2_scale_f16x2(pc[j]);
+      const uint32_t s2 = e4m3x2_scale_f16x2_sel(code_word(pc[j], tq), code_sel);
       ps[j][0] = f16x2_splat_lo(s2);
       ps[j][1] = f16x2_splat_hi(s2);
     }
@@ -792,12 +811,12 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   using I8 = std::integral_constant<int, 8>;
   using I16 = std::integral_constant<int, 16>;
   using I28 = std::integral_constant<int, 28>;
-  auto compute = [&](int kt, auto par) {
+  auto compute = [&](int kt, auto par, auto tqn) {  // tqn: (kt + 1) & 3
     constexpr int P = decltype(par)::value;  // kt & 1
     const v4i* pq = P ? pq1 : pq0;
     uint32_t (*ps)[2] = P ? ps1 : ps0;
     v4i* pqn = P ? pq0 : pq1;
-    uint32_t* pcn = P ? pc0 : pc1;
+    CodeRead* pcn = P ? pc0 : pc1;
     uint32_t (*psn)[2] = P ? ps0 : ps1;
     // slice 0
     mfmas(sf[0], pf[0]);
@@ -816,7 +835,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
     mfmas(sf[0], pf[0]);
     load_shared(kt, 3, sf[1]);
     decode_private(pq, ps, 3, pf[1]);
-    prep_scales(pcn, psn);
+    prep_scales(pcn, psn, tqn);
     slice_groups(I4{}, I28{});
     __builtin_amdgcn_sched_barrier(0);
     // tile kt's reads done; tile kt + 1's shared rows decoded (the data waves' step kt ends here)
@@ -833,15 +852,19 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   read_private(kb, pq0, pc0);
   __builtin_amdgcn_s_waitcnt(0xC07F);
   lds_barrier();  // (2): tile kb's shared rows decoded
+  using T0 = std::integral_constant<int, 0>;
+  using T1 = std::integral_constant<int, 1>;
+  using T2 = std::integral_constant<int, 2>;
+  using T3 = std::integral_constant<int, 3>;
   load_shared(kb, 0, sf[0]);
-  prep_scales(pc0, ps0);
+  prep_scales(pc0, ps0, T0{});
   decode_private(pq0, ps0, 0, pf[0]);
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
 #pragma unroll 1
-  for (int kt = kb; kt < ke; kt += 2) {  // ke - kb is a multiple of 4
-    compute(kt, P0{});
-    compute(kt + 1, P1{});
+  for (int kt = kb; kt < ke; kt += 4) {  // kb and ke are multiples of 4
+    compute(kt, T0{}, T1{});
+    compute(kt + 1, T1{}, T2{});
+    compute(kt + 2, T0{}, T3{});
+    compute(kt + 3, T1{}, T0{});
   }
 
   // Epilogue (as nvfp4_kernel's, TS x TP blocks): SHARED_A: rows m0 + .., columns n0 + 64 wave + ..;
