@@ -333,8 +333,9 @@ def test_log_levels_and_forced_architecture(monkeypatch, capfd):
 
 # NVFP4 small-M problems split K across workgroups (fp32 partials in the plan's workspace, summed in
 # split order by a second kernel); these shapes cover split and unsplit plans, ragged M / N, a final
-# half K tile (K % 64 == 32), and, with K % 256 == 0 (scale codes copied 4 K tiles at a time),
-# 4-tile splits (as long as the copy lead) and splits that start inside a 4-tile group (KT = 76).
+# half K tile (K % 64 == 32), and, with K % 256 == 0 (the warp-specialised kernel: splits take whole
+# 4-tile scale groups), one group in all (K = 256), one group per split (K = 768, 1280) and groups
+# that do not divide evenly over the splits (K = 1792: 7 groups, K = 4864: 19).
 NVFP4_SPLIT_SHAPES = [(100, 80, 1056), (1, 16, 4128), (129, 4000, 2080), (256, 1024, 2048), (640, 4096, 256),
                       (512, 1024, 4096), (300, 2048, 1056), (128, 2048, 1792), (64, 1024, 768), (200, 512, 1280),
                       (96, 2048, 4864)]
