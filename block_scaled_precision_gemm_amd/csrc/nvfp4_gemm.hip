@@ -127,6 +127,34 @@ __device__ __forceinline__ int2 tile_of(int bid, int tiles_m, int tiles_n) {
   return make_int2(first_m + in_group % gsize, in_group / gsize);
 }
 
+// Decoded shared rows (fp16, 128 bytes per row of a K tile): 16-byte piece j of row R sits at
+// position j ^ dec_row_swizzle(R).  16 lanes reading piece j of 16 consecutive rows (16-byte reads
+// resolve 16 lanes per 256 bytes) and 8 lanes storing into 8 consecutive rows (16-byte stores resolve
+// 8 lanes per 128 bytes) both touch distinct banks (measured: no conflict cycles either way, where
+// j ^ ((R >> 1) & 7) left the stores conflicting two ways).
+__device__ __forceinline__ int dec_row_swizzle(int R) { return (R & 7) ^ ((R >> 3) & 1); }
+
+// Row-major scale codes in 16-byte groups (a row's codes of 4 K tiles) are read whole -- 16 lanes'
+// reads of 16 rows' groups are one pass over the banks, where 2-byte reads of 32 rows 16 bytes apart
+// collide four ways -- and the K tile's dword (its 4 codes) picked: at compile time where the tile's
+// place in its group (TQ) is known, else by a select on the run-time index.
+struct RtTq {};  // a K tile's place in its group known at run time only
+template <class TQ>
+struct NextTq { using type = std::integral_constant<int, (TQ::value + 1) & 3>; };
+template <>
+struct NextTq<RtTq> { using type = RtTq; };
+template <class TQ>
+__device__ __forceinline__ uint32_t group_word(v4i q, int kt, TQ) {
+  if constexpr (std::is_same_v<TQ, RtTq>) {
+    const int t = kt & 3;  // wave-uniform
+    return (uint32_t)(t & 2 ? (t & 1 ? q[3] : q[2]) : (t & 1 ? q[1] : q[0]));
+  } else {
+    return (uint32_t)q[TQ::value];
+  }
+}
+// Byte-permute selector of half h's two codes in a dword of a K tile's four (e4m3x2_scale_f16x2_sel).
+__device__ __forceinline__ uint32_t half_code_sel(int h) { return h ? 0x030C020Cu : 0x010C000Cu; }
+
 // Scale-code copy plan SCM:
 // 2: row-major scales with K % 256 == 0: 16 bytes per row for 4 K tiles (one copy per wave covers 64
 //    rows, issued once per 4 K tiles into a two-slot ring).  Each row's codes are a separate piece of
@@ -314,20 +342,29 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   uint32_t sd_out[SD_PIECES];
 #pragma unroll
   for (int d = 0; d < SD_PIECES; ++d)
-    sd_out[d] = (uint32_t)(128 * sd_row + (((4 * sd_h + 2 * sd_sub + d) ^ ((sd_row >> 1) & 7)) << 4));
-  auto decode_shared = [&](int kt, auto check) {
+    sd_out[d] = (uint32_t)(128 * sd_row + (((4 * sd_h + 2 * sd_sub + d) ^ dec_row_swizzle(sd_row)) << 4));
+  // The fp16 scale pair of row R, half h of K tile kt (TQ: kt % 4, when known at compile time).
+  auto scale_f16x2 = [&](int kt, int R, int h, uint32_t row_off, auto check, auto tq) -> uint32_t {
+    if constexpr (SCM == 2) {  // K % 256 == 0: no half tile
+      const v4i g = *(const v4i*)(sring + ((kt >> 2) & 1) * SRING + 16 * R);
+      return e4m3x2_scale_f16x2_sel(group_word(g, kt, tq), half_code_sel(h));
+    } else {
+      return e4m3x2_scale_f16x2(half_scales(scale_pair(scale_at(kt, row_off)), kt, h, check));
+    }
+  };
+  auto decode_shared = [&](int kt, auto check, auto tq) {
     const uint8_t* st = raw + ring(kt) * RAW_STAGE;
     uint8_t* out = dec + (ring(kt) & 1) * DEC_STAGE;
     const v4i q4 = *(const v4i*)(st + sd_raw);  // the row's half
-    const uint32_t codes = half_scales(scale_pair(scale_at(kt, sd_scale)), kt, sd_h, check);
+    const uint32_t s = scale_f16x2(kt, sd_row, sd_h, sd_scale, check, tq);
     if constexpr (BS == 256) {
-      v4i r[4];
-      e2m1x32_scaled_f16(q4, codes, r);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) *(v4i*)(out + sd_out[d]) = r[d];
+      const uint32_t s0 = f16x2_splat_lo(s), s1 = f16x2_splat_hi(s);
+      *(v4i*)(out + sd_out[0]) = e2m1x8_scaled_f16x8((uint32_t)q4[0], s0);
+      *(v4i*)(out + sd_out[1]) = e2m1x8_scaled_f16x8((uint32_t)q4[1], s0);
+      *(v4i*)(out + sd_out[2]) = e2m1x8_scaled_f16x8((uint32_t)q4[2], s1);
+      *(v4i*)(out + sd_out[3]) = e2m1x8_scaled_f16x8((uint32_t)q4[3], s1);
     } else {  // 8 of the half's 16 bytes
       const uint2 q = sd_sub ? make_uint2((uint32_t)q4[2], (uint32_t)q4[3]) : make_uint2((uint32_t)q4[0], (uint32_t)q4[1]);
-      const uint32_t s = e4m3x2_scale_f16x2(codes);
       const uint32_t s2 = sd_sub ? f16x2_splat_hi(s) : f16x2_splat_lo(s);
       *(v4i*)(out + sd_out[0]) = e2m1x8_scaled_f16x8(q.x, s2);
       *(v4i*)(out + sd_out[1]) = e2m1x8_scaled_f16x8(q.y, s2);
@@ -345,7 +382,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   }
   // Shared block i, slice s: decoded row WSH_ROWS wsh + 32i + r, piece 4 hl + s.
   const uint32_t sf_row = (uint32_t)(128 * (WSH_ROWS * wsh + r32));
-  const int sf_sw = (r32 >> 1) & 7;  // (WSH_ROWS wsh + 32i + r) >> 1 & 7 does not depend on wsh, i
+  const int sf_sw = dec_row_swizzle(r32);  // that of row WSH_ROWS wsh + 32i + r: a multiple of 16 plus r
   uint32_t sf_piece[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) sf_piece[s] = (uint32_t)(((4 * hl + s) ^ sf_sw) << 4);
@@ -358,7 +395,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 
   // One K tile: tile kt's private rows are decoded into registers slice by slice, one slice ahead of
   // the MFMAs that use them; tile kt+1's shared rows go to the other decoded buffer.
-  auto step = [&](int kt, auto check) {
+  auto step = [&](int kt, auto check, auto tq) {
     const uint8_t* st = raw + ring(kt) * RAW_STAGE;
     const uint8_t* dst = dec + (ring(kt) & 1) * DEC_STAGE;
     v4i pq[TP];
@@ -366,7 +403,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TP; ++j) {
       pq[j] = *(const v4i*)(st + pf_raw[j]);
-      const uint32_t s = e4m3x2_scale_f16x2(half_scales(scale_pair(scale_at(kt, pf_scale[j])), kt, hl, check));
+      const uint32_t s = scale_f16x2(kt, BS + WP_ROWS * wp + 32 * j + r32, hl, pf_scale[j], check, tq);
       ps[j][0] = f16x2_splat_lo(s);
       ps[j][1] = f16x2_splat_hi(s);
     }
@@ -391,7 +428,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
           acc[i][j] = SHARED_A ? mfma_f16(sf[c][i], pf[c][j], acc[i][j]) : mfma_f16(pf[c][j], sf[c][i], acc[i][j]);
       // tile kt+1's shared rows, decoded behind the first slice's MFMAs rather than ahead of them
       // (4096^3: -3%); past the last tile: stale bytes into a buffer nobody reads
-      if (s == 0) decode_shared(kt + 1, check);
+      if (s == 0) decode_shared(kt + 1, check, typename NextTq<decltype(tq)>::type{});
     }
   };
 
@@ -420,7 +457,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // tile kb (and its codes) landed: tiles kb+1, kb+2 and their groups may stay in flight
   wait_copies_x(std::integral_constant<int, 2 * NCOP>{}, starts_group(kb + 1) || starts_group(kb + 2));
   lds_barrier();  // every wave's copies of tile kb have landed
-  decode_shared(kb, Checked{});
+  decode_shared(kb, Checked{}, RtTq{});
   wait_copies_x(ICN{}, starts_group(kb + 2));
   lds_barrier();  // tile kb decoded, tile kb+1 landed
   // Steady state: step kt issues tile kt+DIST's copies, computes tile kt and decodes tile kt+1's
@@ -429,29 +466,34 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   // Raw stages in use: kt .. kt+DIST: NR = DIST + 1.
   auto single = [&](int kt) {
     copy_tile(kt + DIST, starts_group(kt + DIST));
-    step(kt, Unchecked{});
+    step(kt, Unchecked{}, RtTq{});
     wait_copies_x(ICN{}, starts_group(kt + DIST));
     lds_barrier();
   };
   int kt = kb;
 #pragma unroll 1
   for (; (kt & (NR - 1)) != 0 && kt + DIST < ke; ++kt) single(kt);  // up to a multiple of NR
+  auto unrolled = [&](auto cc) {  // step kt + c with kt == 0 (mod NR): the tile's place in its group is c
+    constexpr int c = decltype(cc)::value;
+    copy_tile(kt + c + DIST, SCM == 2 && ((c + DIST) & 3) == 0);
+    step(kt + c, Unchecked{}, cc);
+    wait_copies_x(ICN{}, SCM == 2 && ((c + DIST) & 3) == 0);
+    lds_barrier();
+  };
+  static_assert(NR == 4, "one scale group per unrolled iteration");
 #pragma unroll 1
   for (; kt + NR - 1 + DIST < ke; kt += NR) {
-#pragma unroll
-    for (int c = 0; c < NR; ++c) {  // kt + c == c (mod NR)
-      copy_tile(kt + c + DIST, SCM == 2 && ((c + DIST) & 3) == 0);
-      step(kt + c, Unchecked{});
-      wait_copies_x(ICN{}, SCM == 2 && ((c + DIST) & 3) == 0);
-      lds_barrier();
-    }
+    unrolled(std::integral_constant<int, 0>{});
+    unrolled(std::integral_constant<int, 1>{});
+    unrolled(std::integral_constant<int, 2>{});
+    unrolled(std::integral_constant<int, 3>{});
   }
 #pragma unroll 1
   for (; kt + DIST < ke; ++kt) single(kt);
   // Last DIST tiles: nothing left to copy.  Leaves no copy in flight past the end of the kernel.
 #pragma unroll 1
   for (; kt < ke; ++kt) {
-    step(kt, Checked{});
+    step(kt, Checked{}, RtTq{});
     wait_copies<0>();
     lds_barrier();
   }
@@ -598,7 +640,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   // Decoded shared rows: 16-byte piece j of row R at 128R + ((j ^ f(R)) << 4), f(R) = (R & 7) ^
   // ((R >> 3) & 1): 16 lanes reading piece j of 16 consecutive rows (256 bytes per pass) and 8
   // lanes storing into 8 consecutive rows (128 bytes per pass) both touch distinct banks.
-  auto dec_swz = [](int R) { return (R & 7) ^ ((R >> 3) & 1); };
+  auto dec_swz = [](int R) { return dec_row_swizzle(R); };
 
   if (wave >= 4) {
     // ---- data waves: copies and the shared rows' decode ------------------------------------------
