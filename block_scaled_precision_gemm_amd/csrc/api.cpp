@@ -56,6 +56,7 @@ int env_log_level() {
 std::mutex g_dev_mutex;
 signed char g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 not
 int g_dev_cus[64];         // compute units of a checked device
+int g_dev_l2[64];          // L2 bytes of one XCD of a checked device
 
 // BSG_FORCE_ARCH naming another architecture: refuse before any device query.
 bsg_status check_forced_arch() {
@@ -88,6 +89,7 @@ bsg_status check_device(int dev) {
     }
     g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     g_dev_cus[dev] = prop.multiProcessorCount;
+    g_dev_l2[dev] = prop.l2CacheSize;
     if (g_dev_ok[dev] < 0) {
       set_error("device %d is %s; this library is built for gfx950 (MI355X) only", dev, prop.gcnArchName);
       return BSG_ERR_DEVICE;
@@ -349,6 +351,8 @@ bsg_status build_plan(const bsg_problem* problem, bsg_plan_s* plan) {
   if (a.splits > 1)
     plan->workspace_bytes =
         (uint64_t)problem->batch * a.splits * (uint64_t)problem->M * (uint64_t)problem->N * sizeof(float);
+  // Partials of at least one L2 per XCD (8 XCDs) are stored through the L2 (splitk.h, store_partials).
+  a.ws_through = a.splits > 1 && g_dev_l2[dev] > 0 && plan->workspace_bytes >= 8ull * (uint64_t)g_dev_l2[dev];
   plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n * a.splits), 1, (unsigned)problem->batch)
                              : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, (unsigned)problem->batch);
   plan->block = dim3((unsigned)v.block_threads, 1, 1);
@@ -359,12 +363,12 @@ bsg_status build_plan(const bsg_problem* problem, bsg_plan_s* plan) {
   plan->log_level = env_log_level();
   if (plan->log_level >= 1)
     fprintf(stderr,
-            "bsg: plan %s M=%lld N=%lld K=%lld batch=%lld -> %s tile %dx%dx%d grid (%u,%u,%u) block %u splits %d "
+            "bsg: plan %s M=%lld N=%lld K=%lld batch=%lld -> %s tile %dx%dx%d grid (%u,%u,%u) block %u splits %d%s "
             "workspace %llu B on device %d\n",
             problem->format == BSG_FMT_MXFP8 ? "mxfp8" : "nvfp4", (long long)problem->M, (long long)problem->N,
             (long long)problem->K, (long long)problem->batch, plan->variant, plan->tile_m, plan->tile_n,
             plan->tile_k, plan->grid.x, plan->grid.y, plan->grid.z, plan->block.x, a.splits,
-            (unsigned long long)plan->workspace_bytes, dev);
+            a.ws_through ? " (partials through L2)" : "", (unsigned long long)plan->workspace_bytes, dev);
   return BSG_OK;
 }
 

@@ -33,6 +33,7 @@ struct GemmArgs {
   int tiles_m, tiles_n;   // output tile grid
   int splits;             // split-K factor (1: none)
   int scale_ktile;        // 0: sA / sB row-major [rows][KB]; 1: K-tile-major [ceil(KB/4)][rows][4]
+  int ws_through;         // NVFP4 split plans: 1 = partial stores write through the L2 (store_partials)
   float* ws;              // split-K partials [batch][splits][M][N] fp32 (plan-owned), or null
   // Batched problems: grid.z = batch count; batch z uses each pointer advanced by z * its stride
   // (bytes; a stride of 0 shares one matrix / bias vector among all batches).

@@ -512,46 +512,57 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   float* stage = (float*)lds + wave * (32 * EPI_STRIDE);
   const int mw = m0 + (SHARED_A ? WSH_ROWS * wsh : WP_ROWS * wp), nw = n0 + (SHARED_A ? WP_ROWS * wp : WSH_ROWS * wsh);
   const float alpha = load_alpha(p) * kRescale;
+  auto write_out = [&](auto through) {
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
+    for (int pass = 0; pass < PASSES; ++pass) {
 #pragma unroll
-    for (int i = 0; i < TS; ++i)
+      for (int i = 0; i < TS; ++i)
 #pragma unroll
-      for (int j = 0; j < TP; ++j) {
-        const int mi = SHARED_A ? i : j, ni = SHARED_A ? j : i;
-        if (mi != pass) continue;
+        for (int j = 0; j < TP; ++j) {
+          const int mi = SHARED_A ? i : j, ni = SHARED_A ? j : i;
+          if (mi != pass) continue;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          stage[(8 * (e >> 2) + 4 * hl + (e & 3)) * EPI_STRIDE + 32 * ni + r32] = acc[i][j][e];
+          for (int e = 0; e < 16; ++e)
+            stage[(8 * (e >> 2) + 4 * hl + (e & 3)) * EPI_STRIDE + 32 * ni + r32] = acc[i][j][e];
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int c4 = 4 * (lane % LPR);
+      const int n = nw + c4;
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = RPI * it + lane / LPR;
+        const int m = mw + 32 * pass + row;
+        const v4f v = *(const v4f*)(stage + row * EPI_STRIDE + c4);
+        if (m >= p.M || n >= p.N) continue;  // N % 16 == 0: a lane's 4 columns are all in or all out
+        if constexpr (SPLIT) {
+          store_partials<decltype(through)::value>(p.ws + (size_t)split * p.M * p.N, (uint32_t)p.M * (uint32_t)p.N * 4u,
+                                                   (uint32_t)m * (uint32_t)p.N + (uint32_t)n, v);
+        } else {
+          v4f b = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
+          uint2 o;
+          o.x = epi_pack2<SILU, O>(v[0], v[1], alpha, b[0], b[1]);
+          o.y = epi_pack2<SILU, O>(v[2], v[3], alpha, b[2], b[3]);
+          *(uint2*)((uint16_t*)p.D + (size_t)m * p.ldd + n) = o;
+        }
       }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int c4 = 4 * (lane % LPR);
-    const int n = nw + c4;
-#pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int row = RPI * it + lane / LPR;
-      const int m = mw + 32 * pass + row;
-      const v4f v = *(const v4f*)(stage + row * EPI_STRIDE + c4);
-      if (m >= p.M || n >= p.N) continue;  // N % 16 == 0: a lane's 4 columns are all in or all out
-      if constexpr (SPLIT) {
-        // streaming store: read once, by the finish kernel
-        __builtin_nontemporal_store(v, (v4f*)(p.ws + (size_t)split * p.M * p.N + (size_t)m * p.N + n));
-      } else {
-        v4f b = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
-        uint2 o;
-        o.x = epi_pack2<SILU, O>(v[0], v[1], alpha, b[0], b[1]);
-        o.y = epi_pack2<SILU, O>(v[2], v[3], alpha, b[2], b[3]);
-        *(uint2*)((uint16_t*)p.D + (size_t)m * p.ldd + n) = o;
-      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass overwrites
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass overwrites
+  };
+  if constexpr (SPLIT) {
+    if (p.ws_through)
+      write_out(std::true_type{});
+    else
+      write_out(std::false_type{});
+  } else {
+    write_out(std::false_type{});
   }
 }
 
-// Warp-specialised variant of the 128-row-shared-side kernel, for K % 256 == 0 (either scale layout).  Waves 4..7 move data: they copy every row global -> LDS two K tiles at a time (64
-// bytes per row and copy: half the row pieces of single-tile copies) and decode the 128 shared rows
-// of the next K tile into a double-buffered fp16 tile.  Waves 0..3 (one per SIMD) compute: wave w
+// Warp-specialised variant of the 128-row-shared-side kernel, for K % 256 == 0 (either scale
+// layout).  Waves 4..7 move data: they copy every row global -> LDS two K tiles at a time (64 bytes
+// per row and copy: half the row pieces of single-tile copies) and decode the 128 shared rows of the
+// next K tile into a double-buffered fp16 tile.  Waves 0..3 (one per SIMD) compute: wave w
 // owns all 128 shared rows and private rows 64w .. 64w+63 (4 x 2 accumulators), reads the shared
 // fragments from the decoded tile and decodes its own private rows from the packed bytes into MFMA
 // operands, as nvfp4_kernel does.  Against eight waves that each take all shared rows and 32
@@ -636,11 +647,8 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
     else
       return (uint32_t)c[decltype(tq)::value];
   };
-  const uint32_t code_sel = hl ? 0x030C020Cu : 0x010C000Cu;  // this lane's half's two codes
-  // Decoded shared rows: 16-byte piece j of row R at 128R + ((j ^ f(R)) << 4), f(R) = (R & 7) ^
-  // ((R >> 3) & 1): 16 lanes reading piece j of 16 consecutive rows (256 bytes per pass) and 8
-  // lanes storing into 8 consecutive rows (128 bytes per pass) both touch distinct banks.
-  auto dec_swz = [](int R) { return dec_row_swizzle(R); };
+  const uint32_t code_sel = half_code_sel(hl);  // this lane's half's two codes
+  // Decoded shared rows: 16-byte piece j of row R at 128R + ((j ^ dec_row_swizzle(R)) << 4).
 
   if (wave >= 4) {
     // ---- data waves: copies and the shared rows' decode ------------------------------------------
@@ -710,7 +718,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
     };
     // Shared decode of K tile t into buffer t & 1: lane l takes shared row 32pw + (l & 31), half
     // l >> 5, and stores its 32 fp16 values as pieces 4h .. 4h+3 of the row.  tq: t & 3.
-    const int sd_row = 32 * pw + r32, sd_swz = dec_swz(sd_row);
+    const int sd_row = 32 * pw + r32, sd_swz = dec_row_swizzle(sd_row);
     auto decode_shared = [&](int kt, auto tq) {
       const v4i q4 = *(const v4i*)raw_at(kt, sd_row, hl);
       const uint32_t s = e4m3x2_scale_f16x2_sel(code_word(read_codes(kt, sd_row), tq), code_sel);
@@ -787,7 +795,7 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
     for (int j = 0; j < TP; ++j) acc[i][j] = v16f{};
   // Shared block i, slice s: decoded row 32i + r, piece (4 hl + s) ^ f(r) (f(32i + r) = f(r)).  Private
   // block j: row BS + 64 wave + 32j + r, the lane's half hl, decoded slice by slice in registers.
-  const int sw = dec_swz(r32);
+  const int sw = dec_row_swizzle(r32);
   uint32_t piece[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) piece[s] = (uint32_t)(((4 * hl + s) ^ sw) << 4);
@@ -916,39 +924,50 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   float* stage = (float*)lds + wave * (32 * EPI_STRIDE);
   const int mw = m0 + (SHARED_A ? 0 : 64 * wave), nw = n0 + (SHARED_A ? 64 * wave : 0);
   const float alpha = load_alpha(p) * kRescale;
+  auto write_out = [&](auto through) {
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
+    for (int pass = 0; pass < PASSES; ++pass) {
 #pragma unroll
-    for (int i = 0; i < TS; ++i)
+      for (int i = 0; i < TS; ++i)
 #pragma unroll
-      for (int j = 0; j < TP; ++j) {
-        const int mi = SHARED_A ? i : j, ni = SHARED_A ? j : i;
-        if (mi != pass) continue;
+        for (int j = 0; j < TP; ++j) {
+          const int mi = SHARED_A ? i : j, ni = SHARED_A ? j : i;
+          if (mi != pass) continue;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          stage[(8 * (e >> 2) + 4 * hl + (e & 3)) * EPI_STRIDE + 32 * ni + r32] = acc[i][j][e];
+          for (int e = 0; e < 16; ++e)
+            stage[(8 * (e >> 2) + 4 * hl + (e & 3)) * EPI_STRIDE + 32 * ni + r32] = acc[i][j][e];
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int c4 = 4 * (lane % LPR);
+      const int n = nw + c4;
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = RPI * it + lane / LPR;
+        const int m = mw + 32 * pass + row;
+        const v4f v = *(const v4f*)(stage + row * EPI_STRIDE + c4);
+        if (m >= p.M || n >= p.N) continue;  // N % 16 == 0: a lane's 4 columns are all in or all out
+        if constexpr (SPLIT) {
+          store_partials<decltype(through)::value>(p.ws + (size_t)split * p.M * p.N, (uint32_t)p.M * (uint32_t)p.N * 4u,
+                                                   (uint32_t)m * (uint32_t)p.N + (uint32_t)n, v);
+        } else {
+          v4f b = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
+          uint2 o;
+          o.x = epi_pack2<SILU, O>(v[0], v[1], alpha, b[0], b[1]);
+          o.y = epi_pack2<SILU, O>(v[2], v[3], alpha, b[2], b[3]);
+          *(uint2*)((uint16_t*)p.D + (size_t)m * p.ldd + n) = o;
+        }
       }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int c4 = 4 * (lane % LPR);
-    const int n = nw + c4;
-#pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int row = RPI * it + lane / LPR;
-      const int m = mw + 32 * pass + row;
-      const v4f v = *(const v4f*)(stage + row * EPI_STRIDE + c4);
-      if (m >= p.M || n >= p.N) continue;  // N % 16 == 0: a lane's 4 columns are all in or all out
-      if constexpr (SPLIT) {
-        __builtin_nontemporal_store(v, (v4f*)(p.ws + (size_t)split * p.M * p.N + (size_t)m * p.N + n));
-      } else {
-        v4f b = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BIAS) b = v4f{p.bias[n], p.bias[n + 1], p.bias[n + 2], p.bias[n + 3]};
-        uint2 o;
-        o.x = epi_pack2<SILU, O>(v[0], v[1], alpha, b[0], b[1]);
-        o.y = epi_pack2<SILU, O>(v[2], v[3], alpha, b[2], b[3]);
-        *(uint2*)((uint16_t*)p.D + (size_t)m * p.ldd + n) = o;
-      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass overwrites
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass overwrites
+  };
+  if constexpr (SPLIT) {
+    if (p.ws_through)
+      write_out(std::true_type{});
+    else
+      write_out(std::false_type{});
+  } else {
+    write_out(std::false_type{});
   }
 }
 

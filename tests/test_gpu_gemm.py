@@ -515,6 +515,22 @@ def test_nvfp4_plan_info():
     assert info["grid"][0] == 256
 
 
+# Split plans whose fp32 partials come to at least one L2 (4 MiB) per XCD store them with
+# device-scope stores, which write through the L2; smaller partial sets use streaming stores.  Both
+# forms against the oracle: the single-tile kernel (K % 256 != 0) and the shared-B warp-specialised
+# kernel with partials stored through, the looped 256x4096x4096 shape (24 MiB) streamed.  The
+# plan's choice is read from its BSG_LOG line.
+@pytest.mark.parametrize("shape,through", [((128, 8192, 8224), True), ((256, 8192, 4096), True),
+                                           ((256, 4096, 4096), False)], ids=lambda v: str(v))
+def test_nvfp4_partial_store_forms(shape, through, monkeypatch, capfd):
+    M, N, K = shape
+    monkeypatch.setenv("BSG_LOG", "1")
+    p = si.problem("nvfp4", M, N, K, seed=M + N + K, bias=True, out="bf16")
+    _check(p, rows=np.unique(np.concatenate([np.arange(0, M, 7), [M - 1]])))
+    log = capfd.readouterr().err
+    assert "splits" in log and ("(partials through L2)" in log) == through, log
+
+
 # NVFP4 grids of at least one 256 x 256 tile per CU: 256 x 256 tiles (B shared: 256 rows decoded per K
 # tile into LDS; 8 waves of 64 x 128).  Ragged M / N, a final half K tile, every epilogue.
 NVFP4_256_SHAPES = [(4096, 4096, 256), (4000, 4112, 1056), (2048, 8192, 512)]
