@@ -34,6 +34,8 @@
 //   [s KT / S, (s+1) KT / S) and writes its raw fp32 accumulators to a plan-owned workspace
 //   [S][M][N]; a second kernel sums the S partials in split order (deterministic), applies the
 //   epilogue and writes D.  With S == 1 the epilogue runs in the GEMM kernel.
+// * With the 128-row shared side and K % 256 == 0 a warp-specialised variant runs instead
+//   (nvfp4_ws_kernel): four waves copy and decode the shared rows, four compute.
 //
 // v_mfma_f32_32x32x16_f16 register layout: A lane l (r = l % 32, h = l / 32) holds row r, K
 // slots [8h, 8h+8) of the 16-slot slice; B likewise for column r; accumulator element e of lane l:
@@ -45,8 +47,8 @@
 //   reads: 16 lanes = 16 rows x one half); the two scale codes of row R, half h at 8R + 4h (a
 //   2-byte buffer_load ... lds fills a 4-byte LDS slot per lane, zero-extended).
 // * decoded shared stage: row R = 128 bytes = 8 pieces of 8 fp16 (piece p = elements 8p .. 8p+7),
-//   piece p stored at p ^ ((R >> 1) & 7) (decode stores: 8 rows x 2 halves per 16 lanes; fragment
-//   reads: 16 rows x one piece).
+//   piece p stored at p ^ dec_row_swizzle(R) (decode stores: 8 rows x 2 halves per 16 lanes;
+//   fragment reads: 16 rows x one piece).
 #include "codec.h"
 #include "common.h"
 #include "epilogue.h"

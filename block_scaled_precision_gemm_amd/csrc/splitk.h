@@ -7,11 +7,13 @@
 // power-of-two factor (the NVFP4 fp16 route: 2^-16).  One thread per 4 consecutive columns
 // (N % 16 == 0); grid.z = batch.
 //
-// LOAD_ALL issues a thread's S partial loads before the first sum: one memory round trip instead of
-// S.  That pays while one partial plane (batch x M x N x 4 bytes, what all threads read per round
-// trip) is smaller than latency x bandwidth (~4 MiB: 0.8 us at ~5 TB/s), where a plane-by-plane
-// pass waits on latency; from there on the plane-by-plane order streams at least as fast (measured:
-// 1-2 MiB planes 5-11% faster with LOAD_ALL, 4 MiB planes 1% slower).
+// DEPTH: the partial loads a thread keeps in flight.  0 issues all S before the first sum: one
+// memory round trip instead of S.  That pays while one partial plane (batch x M x N x 4 bytes, what
+// all threads read per round trip) is smaller than latency x bandwidth (~4 MiB: 0.8 us at ~5 TB/s),
+// where a plane-by-plane pass waits on latency (measured: 1-2 MiB planes 5-11% faster, 4 MiB planes
+// 1% slower).  From 4 MiB planes go by one or two at a time: two for partials the GEMM left in the
+// L2s (256x4096x4096: 2.0-2.6% faster per call than one; three or four at a time slower again),
+// one for partials stored through the L2 (GemmArgs::ws_through; two: +0.6-1.8% at S = 4).
 //
 // TBM x TBN (0 x 0: rows in order): the GEMM kernel put every split of tile t on XCD t % 8
 // (workgroups go to the 8 XCDs round-robin by id), and block b sums part of a tile t with
@@ -59,7 +61,7 @@ struct RowMajorTiles {
   }
 };
 
-template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, bool LOAD_ALL, int TBM = 0, int TBN = 0,
+template <Out O, bool BIAS, bool SILU, int RESCALE_LOG2, int DEPTH, int TBM = 0, int TBN = 0,
           class TileMap = RowMajorTiles>
 __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   select_batch(p);
@@ -86,7 +88,8 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
   // streaming loads: every partial is read exactly once; sums in split order either way
   auto ld = [&](int k) -> v4f { return __builtin_nontemporal_load((const v4f*)(src + k * plane)); };
   v4f s;
-  if constexpr (LOAD_ALL) {
+  static_assert(DEPTH >= 0 && DEPTH <= 2, "load depth");
+  if constexpr (DEPTH == 0) {
     v4f part[kMaxFinishSplits];
 #pragma unroll
     for (int k = 0; k < kMaxFinishSplits; ++k)
@@ -97,7 +100,15 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmArgs p) {
       if (k < p.splits) s += part[k];
   } else {
     s = ld(0);
-    for (int k = 1; k < p.splits; ++k) s += ld(k);
+    int k = 1;
+    if constexpr (DEPTH == 2) {
+      for (; k + 1 < p.splits; k += 2) {
+        const v4f x = ld(k), y = ld(k + 1);
+        s += x;
+        s += y;
+      }
+    }
+    for (; k < p.splits; ++k) s += ld(k);
   }
   const float alpha = load_alpha(p) * (float)(1u << RESCALE_LOG2);
   v4f b = {0.f, 0.f, 0.f, 0.f};
@@ -114,16 +125,22 @@ hipError_t launch_splitk_finish(const GemmArgs& args, unsigned batch, hipStream_
   if (args.splits < 1 || args.splits > kMaxFinishSplits) return hipErrorInvalidValue;
   void* kargs[] = {(void*)&args};
   const int64_t threads = (int64_t)args.M * (args.N >> 2);
-  const bool load_all = 16.0 * (double)threads * (double)batch < 4.0 * 1024 * 1024;  // one plane < 4 MiB
+  const int depth = 16.0 * (double)threads * (double)batch < 4.0 * 1024 * 1024 ? 0  // one plane < 4 MiB
+                    : args.ws_through                                             ? 1
+                                                                                  : 2;
+  auto pick = [&](auto tbm) -> const void* {
+    constexpr int BM = decltype(tbm)::value, BN = BM > 0 ? TBN : 0;
+    return depth == 0   ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, 0, BM, BN, TileMap>
+           : depth == 1 ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, 1, BM, BN, TileMap>
+                        : (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, 2, BM, BN, TileMap>;
+  };
   if constexpr (TBM > 0) {
     const unsigned blocks = (unsigned)(args.tiles_m * args.tiles_n) * (unsigned)(TBM * TBN / 4 / 256);
-    const void* k = load_all ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, true, TBM, TBN, TileMap>
-                             : (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, false, TBM, TBN, TileMap>;
-    return hipLaunchKernel(k, dim3(blocks, 1, batch), dim3(256), kargs, 0, stream);
+    return hipLaunchKernel(pick(std::integral_constant<int, TBM>{}), dim3(blocks, 1, batch), dim3(256), kargs, 0, stream);
+  } else {
+    return hipLaunchKernel(pick(std::integral_constant<int, 0>{}), dim3((unsigned)((threads + 255) / 256), 1, batch),
+                           dim3(256), kargs, 0, stream);
   }
-  const void* k = load_all ? (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, true>
-                           : (const void*)&splitk_finish_kernel<O, BIAS, SILU, RESCALE_LOG2, false>;
-  return hipLaunchKernel(k, dim3((unsigned)((threads + 255) / 256), 1, batch), dim3(256), kargs, 0, stream);
 }
 
 }  // namespace bsg
