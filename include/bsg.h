@@ -161,7 +161,8 @@ typedef struct bsg_plan_info {
  * precompute everything a call needs.  On success *out_plan is a new plan.  Errors: BSG_ERR_NULL,
  * BSG_ERR_ABI, BSG_ERR_SHAPE, BSG_ERR_UNSUPPORTED, BSG_ERR_DEVICE, BSG_ERR_HIP, BSG_ERR_ALLOC.
  * Environment, read here (never by bsg_run): BSG_LOG=1 writes one line per plan to stderr (problem,
- * variant, tile, grid, split factor, workspace); BSG_LOG=2 also one line per run of that plan.
+ * variant, tile, grid, split factor and partial-store form, workspace); BSG_LOG=2 also one line per
+ * run of that plan.
  * BSG_FORCE_ARCH=<name> makes the architecture check see <name>: any name but gfx950 fails with
  * BSG_ERR_DEVICE (checked before the device is queried, so it works without a GPU); gfx950 keeps
  * the check of the real device. */
