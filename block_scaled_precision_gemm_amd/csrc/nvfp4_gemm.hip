@@ -204,8 +204,9 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_kernel(GemmArgs p) {
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int K = p.K, KT = (K + BK - 1) / BK;
-  const int kb = SPLIT ? (int)((int64_t)split * KT / p.splits) : 0;
-  const int ke = SPLIT ? (int)((int64_t)(split + 1) * KT / p.splits) : KT;
+  // (split + 1) * KT < 2^29 (at most 16 splits, K < 2^31): 32-bit unsigned division
+  const int kb = SPLIT ? (int)((uint32_t)split * (uint32_t)KT / (uint32_t)p.splits) : 0;
+  const int ke = SPLIT ? (int)((uint32_t)(split + 1) * (uint32_t)KT / (uint32_t)p.splits) : KT;
   const uint32_t KH = (uint32_t)K >> 1, KS = (uint32_t)K >> 4;
 
   // Buffer resources of the shared and private operand rows of this tile (rows past M / N fall
@@ -619,8 +620,9 @@ __global__ __launch_bounds__(THREADS, 1) void nvfp4_ws_kernel(GemmArgs p) {
   // K % 256 == 0: K tiles come in scale groups of 4, and a split takes whole groups (at least one:
   // the host never splits K into more parts than it has groups)
   const int K = p.K, KG = K / (4 * BK);
-  const int kb = SPLIT ? 4 * (int)((int64_t)split * KG / p.splits) : 0;
-  const int ke = SPLIT ? 4 * (int)((int64_t)(split + 1) * KG / p.splits) : 4 * KG;
+  // (split + 1) * KG < 2^27: 32-bit unsigned division (64-bit took ~400 scalar instructions)
+  const int kb = SPLIT ? 4 * (int)((uint32_t)split * (uint32_t)KG / (uint32_t)p.splits) : 0;
+  const int ke = SPLIT ? 4 * (int)((uint32_t)(split + 1) * (uint32_t)KG / (uint32_t)p.splits) : 4 * KG;
   const uint32_t KH = (uint32_t)K >> 1, KS = (uint32_t)K >> 4;
   const int r32 = lane & 31, hl = lane >> 5;
   // Packed bytes of K tile t, row R (0 .. 383, shared rows first), half h: 16 bytes at

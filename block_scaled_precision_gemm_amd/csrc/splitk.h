@@ -37,9 +37,8 @@ constexpr int kMaxFinishSplits = 16;
 // them.  THROUGH (GemmArgs::ws_through, set at plan time when the partials come to at least one
 // L2's size per XCD): device-scope stores, which write through the L2 to memory.  Kernels choose
 // the form once, outside their store loops (a per-store branch made the compiler wait for each
-// staging read before its store).  Measured per call against streaming
-// stores (interleaved, outputs bit-identical): 4 MiB of partials per XCD 3.3% faster, 3 MiB 0.5%,
-// 2 MiB 3.3% slower.
+// staging read before its store).  Measured per call against streaming stores (interleaved,
+// outputs bit-identical): 4 MiB of partials per XCD 3.3% faster, 3 MiB 0.5%, 2 MiB 3.3% slower.
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 constexpr int kCachePolicySc1 = 16;  // buffer store cache-policy bits: sc1 (device scope)
 template <bool THROUGH>
