@@ -104,3 +104,22 @@ def test_batched_equals_single_calls(fmt, shape):
     for z, (q, D) in enumerate(zip(problems, outs)):
         assert np.array_equal(D, run(q, plan=single)), f"problem {z}"
     single.close()
+
+
+def test_batched_split_partials_through_l2(monkeypatch, capfd):
+    """Two 128x4096x8192 problems split 8 ways: 32 MiB of fp32 partials, one L2 per XCD, so the plan
+    stores them through the L2, each problem's planes in its own workspace slice.  Exact regime:
+    bit for bit against the oracle on sampled rows."""
+    M, N, K, L = 128, 4096, 8192, 2
+    monkeypatch.setenv("BSG_LOG", "1")
+    problems = [exact_regime_problem("nvfp4", M, N, K, seed=7000 + z, out="bf16") for z in range(L)]
+    outs, info = _run_batched(problems, {})
+    log = capfd.readouterr().err
+    assert "(partials through L2)" in log, log
+    splits = info["grid"][0] // (N // info["tile"][1])
+    assert info["workspace_bytes"] == L * splits * M * N * 4 >= 32 << 20, info
+    rows = np.unique(np.concatenate([np.arange(0, M, 9), [M - 1]]))
+    for z, (q, D) in enumerate(zip(problems, outs)):
+        assert not (D == 0x7FFF).any(), f"problem {z}: entries never written"
+        R = reference(q, rows=rows)["bits"]
+        assert np.array_equal(D[rows], R), f"problem {z}: {int((D[rows] != R).sum())} sampled entries differ"
