@@ -351,8 +351,10 @@ bsg_status build_plan(const bsg_problem* problem, bsg_plan_s* plan) {
   if (a.splits > 1)
     plan->workspace_bytes =
         (uint64_t)problem->batch * a.splits * (uint64_t)problem->M * (uint64_t)problem->N * sizeof(float);
-  // Partials of at least one L2 per XCD (8 XCDs) are stored through the L2 (splitk.h, store_partials).
-  a.ws_through = a.splits > 1 && g_dev_l2[dev] > 0 && plan->workspace_bytes >= 8ull * (uint64_t)g_dev_l2[dev];
+  // NVFP4 partials of at least one L2 per XCD (8 XCDs) are stored through the L2 (splitk.h,
+  // store_partials); the MXFP8 tiled kernel always streams its partials.
+  a.ws_through = problem->format == BSG_FMT_NVFP4 && a.splits > 1 && g_dev_l2[dev] > 0 &&
+                 plan->workspace_bytes >= 8ull * (uint64_t)g_dev_l2[dev];
   plan->grid = v.linear_grid ? dim3((unsigned)(a.tiles_m * a.tiles_n * a.splits), 1, (unsigned)problem->batch)
                              : dim3((unsigned)a.tiles_n, (unsigned)a.tiles_m, (unsigned)problem->batch);
   plan->block = dim3((unsigned)v.block_threads, 1, 1);
