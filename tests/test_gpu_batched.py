@@ -60,6 +60,7 @@ def _share(problems, keys):
     ("nvfp4", (1024, 1024, 512), 16),   # ... and the 256 x 256 NVFP4 kernel
     ("nvfp4", (128, 1024, 4096), 2),    # split-K with one workspace slice per problem
     ("nvfp4", (128, 2048, 4096), 2),    # ... with 8 tiles: each tile's splits and finish on one XCD
+    ("nvfp4", (128, 4096, 4096), 2),    # ... 4 MiB planes of streamed partials: two finish loads in flight
     ("mxfp8", (128, 1024, 4096), 2),    # (8 tiles of 128 x 128: the same placement)
 ], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_batched_exact_regime_bit_exact(fmt, shape, L):
